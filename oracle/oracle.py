@@ -1,0 +1,158 @@
+"""Python entry to the double-precision CPU oracle (``rnn_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library or its binding.  The oracle
+shares no code with the HIP path; the only thing both sides see is the layer
+description and the seeded input arrays.
+
+``run(spec, tensors)`` evaluates an ONNX RNN / GRU / LSTM layer as the
+"Recurrent layers" page of the OneGpu docs and the ONNX operator definitions
+describe it (see ``rnn_oracle.c`` for the passages followed), in float64, and
+returns ``{"Y", "Y_h", "Y_c"}`` as float64 arrays.  Inputs of any float dtype
+are widened to float64 exactly (f16 and f32 widen without rounding).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rnn_oracle.c")
+_LIB = os.path.join(_HERE, "librnn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_CELLS = {"RNN": 0, "GRU": 1, "LSTM": 2}
+_DIRS = {"forward": 0, "reverse": 1, "bidirectional": 2}
+_ACTS = {
+    "Relu": 0, "Tanh": 1, "Sigmoid": 2, "Affine": 3, "LeakyRelu": 4, "ThresholdedRelu": 5,
+    "ScaledTanh": 6, "HardSigmoid": 7, "Elu": 8, "Softsign": 9, "Softplus": 10,
+}
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("cell", ctypes.c_int), ("direction", ctypes.c_int), ("layout", ctypes.c_int),
+        ("seq", ctypes.c_int64), ("batch", ctypes.c_int64), ("input", ctypes.c_int64),
+        ("hidden", ctypes.c_int64), ("clip", ctypes.c_double), ("input_forget", ctypes.c_int),
+        ("linear_before_reset", ctypes.c_int), ("max_length", ctypes.c_int64),
+        ("act_kind", ctypes.c_int * 6), ("act_alpha", ctypes.c_double * 6),
+        ("act_beta", ctypes.c_double * 6),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP over independent sequences)."""
+    with _lock:
+        if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            tmp = _LIB + ".tmp%d" % os.getpid()
+            subprocess.check_call([
+                "gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                "-Wall", "-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_rnn.restype = ctypes.c_int
+        lib.oracle_rnn.argtypes = [ctypes.POINTER(_Problem), dp, dp, dp, dp,
+                                   ctypes.POINTER(ctypes.c_int32), dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.oracle_projection.restype = None
+        lib.oracle_projection.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, dp, dp, dp]
+        lib.oracle_activation.restype = ctypes.c_double
+        lib.oracle_activation.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a), dtype=np.float64)
+
+
+def _ptr(a, ctype=ctypes.c_double):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def activation(name: str, alpha: float, beta: float, x: float) -> float:
+    """One activation of the ONNX list, in double."""
+    return _load().oracle_activation(_ACTS[name], alpha, beta, float(x))
+
+
+def projection(A, Bt):
+    """C = A . Bt^T in double (A [M,K], Bt [N,K])."""
+    A = _f64(A)
+    Bt = _f64(Bt)
+    M, K = A.shape
+    N = Bt.shape[0]
+    C = np.empty((M, N), dtype=np.float64)
+    _load().oracle_projection(M, N, K, _ptr(A), _ptr(Bt), _ptr(C))
+    return C
+
+
+def run(spec, tensors: dict, nthreads: int = 0, outputs=None) -> dict:
+    """Evaluate one layer.
+
+    ``spec`` has the attributes of ``onnx_recurrent_layers_amd.synth.LayerSpec``
+    (cell, direction, layout, seq, batch, input, hidden, clip, input_forget,
+    linear_before_reset, max_length, and ``activations``: the resolved
+    (name, alpha, beta) list, forward slots then reverse slots).
+    ``tensors`` maps X, W, R and optionally B, sequence_lens, initial_h,
+    initial_c, P to arrays in ONNX shapes.  Returns float64 Y, Y_h, Y_c
+    (Y_c only for an LSTM) and the thread count used as ``threads``.
+    """
+    lib = _load()
+    S, Bn, I, H = int(spec.seq), int(spec.batch), int(spec.input), int(spec.hidden)
+    D = 2 if spec.direction == "bidirectional" else 1
+    acts = list(spec.activations)
+    p = _Problem()
+    p.cell = _CELLS[spec.cell]
+    p.direction = _DIRS[spec.direction]
+    p.layout = int(spec.layout)
+    p.seq, p.batch, p.input, p.hidden = S, Bn, I, H
+    p.clip = float(spec.clip) if spec.clip is not None else 0.0
+    p.input_forget = int(spec.input_forget)
+    p.linear_before_reset = int(spec.linear_before_reset)
+    p.max_length = int(spec.max_length or 0)
+    for i, (name, a, b) in enumerate(acts):
+        p.act_kind[i] = _ACTS[name]
+        p.act_alpha[i] = float(a)
+        p.act_beta[i] = float(b)
+
+    X = _f64(tensors["X"])
+    W = _f64(tensors["W"])
+    R = _f64(tensors["R"])
+    Bb = _f64(tensors.get("B"))
+    P = _f64(tensors.get("P"))
+    ih = _f64(tensors.get("initial_h"))
+    ic = _f64(tensors.get("initial_c"))
+    lens = tensors.get("sequence_lens")
+    if lens is not None:
+        lens = np.ascontiguousarray(np.asarray(lens), dtype=np.int32)
+    want = set(outputs) if outputs is not None else {"Y", "Y_h", "Y_c"}
+    if spec.layout == 0:
+        yshape, sshape = (S, D, Bn, H), (D, Bn, H)
+    else:
+        yshape, sshape = (Bn, S, D, H), (Bn, D, H)
+    # outputs start as NaN so that an element the oracle fails to write shows up
+    Y = np.full(yshape, np.nan) if "Y" in want else None
+    Yh = np.full(sshape, np.nan) if "Y_h" in want else None
+    Yc = np.full(sshape, np.nan) if ("Y_c" in want and spec.cell == "LSTM") else None
+    used = lib.oracle_rnn(ctypes.byref(p), _ptr(X), _ptr(W), _ptr(R), _ptr(Bb),
+                          _ptr(lens, ctypes.c_int32), _ptr(ih), _ptr(ic), _ptr(P),
+                          _ptr(Y), _ptr(Yh), _ptr(Yc), int(nthreads))
+    if used < 0:
+        raise ValueError("oracle rejected the layer description")
+    return {"Y": Y, "Y_h": Yh, "Y_c": Yc, "threads": used}
