@@ -1,0 +1,180 @@
+/*
+ * rnn.h -- C ABI of the MI355X (gfx950) library for ONNX recurrent layers:
+ * RNN, GRU and LSTM; forward, reverse and bidirectional; layouts 0 and 1;
+ * sequence_lens; initial states; peepholes; clip; input_forget;
+ * linear_before_reset; the eleven ONNX activations.
+ *
+ * The operations are those of the "Recurrent layers" page of the OneGpu docs
+ * (recursiveai.org/onegpu/docs/recurrent): the problem description and its
+ * checks (introduction and "Scratch"), the four stages of a layer ("How a
+ * layer runs"), the arithmetic order ("Arithmetic and determinism") and the
+ * edge rules ("Semantics"), with tensor shapes from the ONNX operator
+ * definitions the page defers to.
+ *
+ * Conventions
+ *   - Every float tensor of one layer has the same element type, f32 or f16
+ *     (IEEE binary16).  Arithmetic and the recurrent state are f32; f16
+ *     outputs are rounded to nearest even once.
+ *   - Tensors are device pointers plus an element offset (rnn_tensor).  The
+ *     address ptr + elem_offset * element_size must be aligned to the element
+ *     size; no other alignment is required.  Outputs whose pointer is NULL are
+ *     not written; nothing outside an output's extent is ever written.
+ *   - W, R, B and P are read exactly as ONNX stores them (gate blocks i,o,f,c
+ *     for an LSTM, z,r,h for a GRU); nothing is repacked.
+ *   - All memory is owned by the caller.  rnn_encode allocates nothing and
+ *     synchronises nothing: it enqueues kernels on the caller's HIP stream and
+ *     returns.  Each call uses its scratch buffers exclusively until the
+ *     stream has finished the call's work.
+ *   - Errors: a non-zero rnn_status; rnn_last_error() then returns a message
+ *     naming the cell (LSTM, GRU or RNN) and the offending argument.  When any
+ *     check fails, nothing has been enqueued.
+ */
+#ifndef ONNX_RNN_MI355X_H
+#define ONNX_RNN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RNN_OK = 0,
+  RNN_ERR_ARG = 1,         /* a NULL or malformed argument, an option on the wrong cell */
+  RNN_ERR_SHAPE = 2,       /* a negative or overflowing size, a bad max_length */
+  RNN_ERR_UNSUPPORTED = 3, /* a valid layer this build cannot run (limits below) */
+  RNN_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} rnn_status;
+
+typedef enum { RNN_CELL_RNN = 0, RNN_CELL_GRU = 1, RNN_CELL_LSTM = 2 } rnn_cell;
+typedef enum { RNN_DTYPE_F32 = 0, RNN_DTYPE_F16 = 1 } rnn_dtype;
+typedef enum { RNN_DIR_FORWARD = 0, RNN_DIR_REVERSE = 1, RNN_DIR_BIDIRECTIONAL = 2 } rnn_direction;
+
+/* The eleven ONNX activations (operator definitions):
+ *   Relu max(0,x); Tanh; Sigmoid 1/(1+e^-x); Affine a*x+b; LeakyRelu x>=0 ? x : a*x;
+ *   ThresholdedRelu x>a ? x : 0; ScaledTanh a*tanh(b*x); HardSigmoid min(max(a*x+b,0),1);
+ *   Elu x>=0 ? x : a*(e^x-1); Softsign x/(1+|x|); Softplus log(1+e^x). */
+typedef enum {
+  RNN_ACT_RELU = 0, RNN_ACT_TANH = 1, RNN_ACT_SIGMOID = 2, RNN_ACT_AFFINE = 3,
+  RNN_ACT_LEAKY_RELU = 4, RNN_ACT_THRESHOLDED_RELU = 5, RNN_ACT_SCALED_TANH = 6,
+  RNN_ACT_HARD_SIGMOID = 7, RNN_ACT_ELU = 8, RNN_ACT_SOFTSIGN = 9, RNN_ACT_SOFTPLUS = 10
+} rnn_activation_kind;
+
+/* One activation with its alpha and beta already resolved by the caller (the
+ * page's GpuRecurrentActivation): defaults of ONNX are not applied here. */
+typedef struct {
+  int32_t kind;  /* rnn_activation_kind */
+  float alpha;
+  float beta;
+} rnn_activation;
+
+/* Step-engine choice.  AUTO picks per problem from measured speed. */
+typedef enum {
+  RNN_ENGINE_AUTO = 0,
+  RNN_ENGINE_LAUNCH = 1,      /* one kernel launch per step (two for GRU linear_before_reset=0) */
+  RNN_ENGINE_PERSISTENT = 2   /* one cooperative launch for all steps (small batches) */
+} rnn_engine;
+
+/* Layer description (the page's RecurrentProblem plus ONNX attributes). */
+typedef struct {
+  int32_t cell;                /* rnn_cell */
+  int32_t dtype;               /* rnn_dtype: the type of every float tensor */
+  int32_t direction;           /* rnn_direction */
+  int32_t layout;              /* 0: X [S,B,I], states [D,B,H], Y [S,D,B,H]; 1: X [B,S,I], states [B,D,H], Y [B,S,D,H] */
+  int64_t seq;                 /* S >= 0 */
+  int64_t batch;               /* B >= 0 */
+  int64_t input;               /* I >= 0 */
+  int64_t hidden;              /* H >= 1 */
+  float clip;                  /* clamp every gate pre-activation to [-clip, clip] when clip > 0; NaN passes */
+  int32_t input_forget;        /* LSTM only: 0 or 1 (forget gate f = 1 - i) */
+  int32_t linear_before_reset; /* GRU only: 0 or 1 */
+  int32_t num_activations;     /* slots x directions: LSTM 3 (f,g,h), GRU 2 (f,g), RNN 1 (f) per direction */
+  rnn_activation activations[6]; /* forward slots, then reverse slots */
+  int64_t max_length;          /* 0: S.  Otherwise a host-side bound on the sequence lengths (<= S):
+                                  only that many steps run, and longer rows are cut to it */
+  int32_t engine;              /* rnn_engine hint */
+} rnn_problem_desc;
+
+/* Opaque, immutable after creation; safe to share between threads. */
+typedef struct rnn_problem rnn_problem;
+
+/* A device buffer plus an element offset (the page's GpuTensorRef). */
+typedef struct {
+  void* ptr;            /* device pointer, or NULL for an absent tensor */
+  int64_t elem_offset;  /* >= 0, in elements of the tensor's type */
+} rnn_tensor;
+
+/* Operands in ONNX shapes (D = 2 for bidirectional, else 1; G = 4 LSTM, 3 GRU, 1 RNN):
+ *   X [S,B,I] (layout 1: [B,S,I])      required
+ *   W [D, G*H, I]                      required
+ *   R [D, G*H, H]                      required
+ *   B [D, 2*G*H] = Wb then Rb          optional (zeros)
+ *   sequence_lens [B] int32            optional (all S); values above S act as S, below 0 as 0
+ *   initial_h [D,B,H] (layout 1: [B,D,H])  optional (zeros)
+ *   initial_c  same shape, LSTM only   optional (zeros)
+ *   P [D, 3*H] (i, o, f), LSTM only    optional (no peepholes)
+ *   Y [S,D,B,H] (layout 1: [B,S,D,H])  optional output
+ *   Y_h [D,B,H] (layout 1: [B,D,H])    optional output
+ *   Y_c  same shape, LSTM only         optional output */
+typedef struct {
+  rnn_tensor X, W, R, B, sequence_lens, initial_h, initial_c, P, Y, Y_h, Y_c;
+} rnn_operands;
+
+/* Validate a description (64-bit checked arithmetic) and build the immutable
+ * problem.  On success *out owns the problem; free it with
+ * rnn_problem_destroy.  On error *out is set to NULL. */
+int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** out);
+
+/* Free a problem (NULL is ignored). */
+void rnn_problem_destroy(rnn_problem* problem);
+
+/* Scratch the caller must supply to rnn_encode (the page's "Scratch"):
+ *   *xw_bytes    = 4 * D * S * B * G * H: the f32 input projection, laid out
+ *                  time-major [D][S][B][G*H] (row t*B+b of direction d holds
+ *                  X[t,b,:] . W[d]^T);
+ *   *state_bytes = the f32 hidden state after every step, the cell state,
+ *                  and the persistent engine's exchange words.
+ * Either may be 0 (then the matching pointer may be NULL).  Both buffers must
+ * be 256-byte aligned; they may be two regions of one arena. */
+int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state_bytes);
+
+/* Enqueue one layer on `stream` (a hipStream_t; NULL is the default stream).
+ * Stages: the input projection, the state setup, the recurrent steps, and one
+ * output pass for whichever of Y, Y_h, Y_c is requested.  Batch = 0 enqueues
+ * nothing; Seq = 0 writes only Y_h / Y_c (initial states or zeros).  All
+ * checks run before the first launch; on error nothing is enqueued.
+ * sequence_lens is read on the device and not validated there. */
+int rnn_encode(const rnn_problem* problem, const rnn_operands* operands,
+               void* xw_scratch, void* state_scratch, void* stream);
+
+/* rnn_encode with timing marks: the same launches, plus hipEventRecord of
+ * events[i] (a hipEvent_t, or NULL to skip that mark) on `stream` at the
+ * stage boundaries: [0] before the projection, [1] before the state setup,
+ * [2] before the recurrent steps, [3] before the output pass, [4] after it.
+ * Lets a caller time each stage with events on the stream the kernels run on. */
+int rnn_encode_timed(const rnn_problem* problem, const rnn_operands* operands,
+                     void* xw_scratch, void* state_scratch, void* stream, void* const events[5]);
+
+/* Host-side check of sequence lengths (the page asks callers to validate them
+ * on the host): every value in [0, seq].  On success *max_len_out (if not
+ * NULL) receives the largest length, usable as max_length. */
+int rnn_validate_lengths(const int32_t* host_lens, int64_t batch, int64_t seq, int64_t* max_len_out);
+
+/* What rnn_encode will launch for this problem. */
+typedef struct {
+  int32_t engine;          /* rnn_engine actually used */
+  int32_t steps;           /* number of recurrent steps run (max_length or S) */
+  int32_t launches;        /* kernel launches per rnn_encode */
+  int32_t step_blocks;     /* workgroups of the step kernel */
+} rnn_plan_info;
+int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* rnn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONNX_RNN_MI355X_H */

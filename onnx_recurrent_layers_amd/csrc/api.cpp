@@ -1,0 +1,418 @@
+// api.cpp -- the C ABI: validation, planning, scratch sizing and the launch
+// sequence of one layer ("Recurrent layers" page, "How a layer runs": input
+// projection, state setup, the recurrent steps, the output passes).
+//
+// Every check runs in 64-bit checked arithmetic before anything is enqueued
+// (the page's "Scratch" paragraph); messages name the cell and the argument.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "plan.h"
+
+using namespace rnnhip;
+
+namespace {
+
+thread_local std::string g_error;
+
+const char* cell_name(int cell) {
+  switch (cell) {
+    case RNN_CELL_LSTM: return "LSTM";
+    case RNN_CELL_GRU: return "GRU";
+    case RNN_CELL_RNN: return "RNN";
+    default: return "RNN layer";
+  }
+}
+
+int fail(int code, int cell, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = std::string(cell_name(cell)) + ": " + buf;
+  return code;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+  int64_t t;
+  return mul_ok(a, b, &t) && mul_ok(t, c, out);
+}
+
+bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
+  int64_t t;
+  return mul3(a, b, c, &t) && mul_ok(t, d, out);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Largest tensor byte count accepted: keeps every offset computation far from
+// 64-bit overflow.
+constexpr int64_t kMaxBytes = int64_t(1) << 52;
+
+}  // namespace
+
+extern "C" const char* rnn_last_error(void) { return g_error.c_str(); }
+
+extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** out) {
+  g_error.clear();
+  if (out) *out = nullptr;
+  if (!desc) return fail(RNN_ERR_ARG, -1, "desc: NULL");
+  const int cell = desc->cell;
+  if (!out) return fail(RNN_ERR_ARG, cell, "out: NULL");
+  if (cell != RNN_CELL_RNN && cell != RNN_CELL_GRU && cell != RNN_CELL_LSTM)
+    return fail(RNN_ERR_ARG, cell, "cell: unknown value %d", cell);
+  if (desc->dtype != RNN_DTYPE_F32 && desc->dtype != RNN_DTYPE_F16)
+    return fail(RNN_ERR_ARG, cell, "dtype: unknown value %d", desc->dtype);
+  if (desc->direction < RNN_DIR_FORWARD || desc->direction > RNN_DIR_BIDIRECTIONAL)
+    return fail(RNN_ERR_ARG, cell, "direction: unknown value %d", desc->direction);
+  if (desc->layout != 0 && desc->layout != 1)
+    return fail(RNN_ERR_ARG, cell, "layout: must be 0 or 1, got %d", desc->layout);
+  if (desc->seq < 0) return fail(RNN_ERR_SHAPE, cell, "seq: negative (%lld)", (long long)desc->seq);
+  if (desc->batch < 0) return fail(RNN_ERR_SHAPE, cell, "batch: negative (%lld)", (long long)desc->batch);
+  if (desc->input < 0) return fail(RNN_ERR_SHAPE, cell, "input: negative (%lld)", (long long)desc->input);
+  if (desc->hidden < 1) return fail(RNN_ERR_SHAPE, cell, "hidden: must be at least 1 (%lld)", (long long)desc->hidden);
+  if (std::isnan(desc->clip)) return fail(RNN_ERR_ARG, cell, "clip: NaN");
+  if (desc->input_forget != 0 && desc->input_forget != 1)
+    return fail(RNN_ERR_ARG, cell, "input_forget: must be 0 or 1");
+  if (desc->input_forget && cell != RNN_CELL_LSTM)
+    return fail(RNN_ERR_ARG, cell, "input_forget: only an LSTM takes input_forget");
+  if (desc->linear_before_reset != 0 && desc->linear_before_reset != 1)
+    return fail(RNN_ERR_ARG, cell, "linear_before_reset: must be 0 or 1");
+  if (desc->linear_before_reset && cell != RNN_CELL_GRU)
+    return fail(RNN_ERR_ARG, cell, "linear_before_reset: only a GRU takes linear_before_reset");
+  if (desc->engine < RNN_ENGINE_AUTO || desc->engine > RNN_ENGINE_PERSISTENT)
+    return fail(RNN_ERR_ARG, cell, "engine: unknown value %d", desc->engine);
+
+  Problem* p = new (std::nothrow) Problem();
+  if (!p) return fail(RNN_ERR_ARG, cell, "out of host memory");
+  p->desc = *desc;
+  p->G = cell == RNN_CELL_LSTM ? 4 : (cell == RNN_CELL_GRU ? 3 : 1);
+  p->slots = cell == RNN_CELL_LSTM ? 3 : (cell == RNN_CELL_GRU ? 2 : 1);
+  p->D = desc->direction == RNN_DIR_BIDIRECTIONAL ? 2 : 1;
+  p->S = desc->seq;
+  p->B = desc->batch;
+  p->I = desc->input;
+  p->H = desc->hidden;
+  p->esize = desc->dtype == RNN_DTYPE_F32 ? 4 : 2;
+
+  auto bad = [&](int code, const char* fmt, auto... args) {
+    delete p;
+    return fail(code, cell, fmt, args...);
+  };
+  if (desc->num_activations != p->slots * p->D)
+    return bad(RNN_ERR_ARG, "activations: expected %d (slots x directions), got %d", p->slots * p->D,
+               desc->num_activations);
+  for (int i = 0; i < desc->num_activations; ++i)
+    if (desc->activations[i].kind < RNN_ACT_RELU || desc->activations[i].kind > RNN_ACT_SOFTPLUS)
+      return bad(RNN_ERR_ARG, "activations[%d]: unknown kind %d", i, desc->activations[i].kind);
+  if (desc->max_length < 0 || desc->max_length > desc->seq)
+    return bad(RNN_ERR_SHAPE, "max_length: must be in [0, seq], got %lld", (long long)desc->max_length);
+  p->steps = desc->max_length > 0 ? desc->max_length : desc->seq;
+  if (p->H > (int64_t(1) << 24)) return bad(RNN_ERR_UNSUPPORTED, "hidden: above 16777216");
+  if (p->B > (int64_t(1) << 30)) return bad(RNN_ERR_UNSUPPORTED, "batch: above 2^30");
+  if (p->S > (int64_t(1) << 30)) return bad(RNN_ERR_UNSUPPORTED, "seq: above 2^30");
+
+  // Tensor sizes in checked 64-bit arithmetic.
+  int64_t n;
+  const int64_t GH = p->G * p->H;
+  if (!mul3(p->S, p->B, p->I, &n) || !mul_ok(n, p->esize, &n) || n > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "X: size overflows");
+  if (!mul3(p->D, GH, p->I, &n) || !mul_ok(n, p->esize, &n) || n > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "W: size overflows");
+  if (!mul3(p->D, GH, p->H, &n) || !mul_ok(n, p->esize, &n) || n > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "R: size overflows");
+  if (!mul4(p->S, p->D, p->B, p->H, &n) || !mul_ok(n, p->esize, &n) || n > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "Y: size overflows");
+  int64_t xw;
+  if (!mul4(p->D, p->S, p->B, GH, &xw) || !mul_ok(xw, 4, &xw) || xw > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "xw scratch: size overflows");
+  p->xw_bytes = (p->S > 0 && p->B > 0) ? size_t(xw) : 0;
+  int64_t dbh;
+  if (!mul3(p->D, p->B, p->H, &dbh) || dbh > kMaxBytes / 8) return bad(RNN_ERR_SHAPE, "state: size overflows");
+  int64_t slab;
+  if (!mul_ok(p->steps + 1, dbh, &slab) || !mul_ok(slab, 4, &slab) || slab > kMaxBytes)
+    return bad(RNN_ERR_SHAPE, "state scratch: size overflows");
+  StateLayout& st = p->st;
+  size_t off = 0;
+  st.slab = off;  off = align256(off + size_t(slab));
+  st.cell = off;  off = align256(off + size_t(dbh) * 4);
+  st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+  st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+
+  // Engine choice.
+  int blocks = 0, units = 0, wpd = 0;
+  const bool pers_ok = persistent_supported(*p, &blocks, &units, &wpd);
+  int engine = desc->engine;
+  if (engine == RNN_ENGINE_AUTO) engine = pers_ok ? RNN_ENGINE_PERSISTENT : RNN_ENGINE_LAUNCH;
+  if (engine == RNN_ENGINE_PERSISTENT && !pers_ok)
+    return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
+  p->engine = engine;
+  if (engine == RNN_ENGINE_PERSISTENT) {
+    p->pers_blocks = blocks;
+    p->pers_units = units;
+    p->pers_wg_per_dir = wpd;
+    st.xch = off;  off = align256(off + 2 * size_t(dbh) * 8);
+    st.xch2 = off; off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
+  } else {
+    st.xch = st.xch2 = off;
+  }
+  st.total = p->B > 0 ? off : 0;
+
+  *out = reinterpret_cast<rnn_problem*>(p);
+  return RNN_OK;
+}
+
+extern "C" void rnn_problem_destroy(rnn_problem* problem) { delete reinterpret_cast<Problem*>(problem); }
+
+extern "C" int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state_bytes) {
+  g_error.clear();
+  if (!problem) return fail(RNN_ERR_ARG, -1, "problem: NULL");
+  const Problem* p = reinterpret_cast<const Problem*>(problem);
+  if (xw_bytes) *xw_bytes = p->xw_bytes;
+  if (state_bytes) *state_bytes = p->st.total;
+  return RNN_OK;
+}
+
+extern "C" int rnn_validate_lengths(const int32_t* host_lens, int64_t batch, int64_t seq, int64_t* max_len_out) {
+  g_error.clear();
+  if (batch < 0) return fail(RNN_ERR_SHAPE, -1, "sequence_lens: negative batch");
+  if (batch > 0 && !host_lens) return fail(RNN_ERR_ARG, -1, "sequence_lens: NULL");
+  int64_t mx = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    if (host_lens[b] < 0 || host_lens[b] > seq)
+      return fail(RNN_ERR_SHAPE, -1, "sequence_lens[%lld]: %d outside [0, %lld]", (long long)b, host_lens[b],
+                  (long long)seq);
+    if (host_lens[b] > mx) mx = host_lens[b];
+  }
+  if (max_len_out) *max_len_out = mx;
+  return RNN_OK;
+}
+
+namespace {
+
+int step_launch_count(const Problem& p) {
+  if (p.engine == RNN_ENGINE_PERSISTENT) return p.steps > 0 ? 1 : 0;
+  const int per = (p.desc.cell == RNN_CELL_GRU && !p.desc.linear_before_reset) ? 2 : 1;
+  return int(p.steps) * per;
+}
+
+}  // namespace
+
+extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info) {
+  g_error.clear();
+  if (!problem || !info) return fail(RNN_ERR_ARG, -1, "problem/info: NULL");
+  const Problem* p = reinterpret_cast<const Problem*>(problem);
+  info->engine = p->engine;
+  info->steps = int32_t(p->steps);
+  info->step_blocks = p->engine == RNN_ENGINE_PERSISTENT ? p->pers_blocks : 0;
+  int n = 0;
+  if (p->B > 0) {
+    if (p->S > 0) n += 1;          // projection
+    n += 1;                        // state setup
+    if (p->S > 0) n += step_launch_count(*p);
+    n += 1;                        // outputs (one kernel covers Y, Y_h, Y_c)
+  }
+  info->launches = n;
+  return RNN_OK;
+}
+
+namespace {
+
+// Resolve one tensor to a byte pointer, checking alignment and offset.
+int resolve(const rnn_tensor& t, int esize, int cell, const char* name, bool required, const char** out) {
+  *out = nullptr;
+  if (!t.ptr) {
+    if (required) return fail(RNN_ERR_ARG, cell, "%s: NULL", name);
+    return RNN_OK;
+  }
+  if (t.elem_offset < 0) return fail(RNN_ERR_ARG, cell, "%s: negative element offset", name);
+  if (t.elem_offset > kMaxBytes / esize) return fail(RNN_ERR_SHAPE, cell, "%s: element offset overflows", name);
+  const char* base = static_cast<const char*>(t.ptr) + t.elem_offset * esize;
+  if (reinterpret_cast<uintptr_t>(base) % uintptr_t(esize) != 0)
+    return fail(RNN_ERR_ARG, cell, "%s: address not aligned to its %d-byte element", name, esize);
+  *out = base;
+  return RNN_OK;
+}
+
+}  // namespace
+
+namespace {
+
+int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
+                void* stream, void* const* events);
+
+}  // namespace
+
+extern "C" int rnn_encode(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch,
+                          void* state_scratch, void* stream) {
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr);
+}
+
+extern "C" int rnn_encode_timed(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch,
+                                void* state_scratch, void* stream, void* const events[5]) {
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, events);
+}
+
+namespace {
+
+int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
+                void* stream, void* const* events) {
+  g_error.clear();
+  if (!problem) return fail(RNN_ERR_ARG, -1, "problem: NULL");
+  const Problem& p = *reinterpret_cast<const Problem*>(problem);
+  const int cell = p.desc.cell;
+  if (!ops) return fail(RNN_ERR_ARG, cell, "operands: NULL");
+  const bool lstm = cell == RNN_CELL_LSTM;
+  if (!lstm && ops->initial_c.ptr) return fail(RNN_ERR_ARG, cell, "initial_c: only an LSTM takes initial_c");
+  if (!lstm && ops->P.ptr) return fail(RNN_ERR_ARG, cell, "P: only an LSTM takes peepholes");
+  if (!lstm && ops->Y_c.ptr) return fail(RNN_ERR_ARG, cell, "Y_c: only an LSTM has Y_c");
+
+  const int es = p.esize;
+  const char *X, *W, *R, *Bp, *lens, *ih, *ic, *P, *Y, *Yh, *Yc;
+  int rc;
+  if ((rc = resolve(ops->X, es, cell, "X", true, &X))) return rc;
+  if ((rc = resolve(ops->W, es, cell, "W", true, &W))) return rc;
+  if ((rc = resolve(ops->R, es, cell, "R", true, &R))) return rc;
+  if ((rc = resolve(ops->B, es, cell, "B", false, &Bp))) return rc;
+  if ((rc = resolve(ops->sequence_lens, 4, cell, "sequence_lens", false, &lens))) return rc;
+  if ((rc = resolve(ops->initial_h, es, cell, "initial_h", false, &ih))) return rc;
+  if ((rc = resolve(ops->initial_c, es, cell, "initial_c", false, &ic))) return rc;
+  if ((rc = resolve(ops->P, es, cell, "P", false, &P))) return rc;
+  if ((rc = resolve(ops->Y, es, cell, "Y", false, &Y))) return rc;
+  if ((rc = resolve(ops->Y_h, es, cell, "Y_h", false, &Yh))) return rc;
+  if ((rc = resolve(ops->Y_c, es, cell, "Y_c", false, &Yc))) return rc;
+
+  if (p.B == 0) return RNN_OK;  // nothing is recorded
+  if (p.xw_bytes > 0) {
+    if (!xw_scratch) return fail(RNN_ERR_ARG, cell, "xw_scratch: NULL (needs %zu bytes)", p.xw_bytes);
+    if (reinterpret_cast<uintptr_t>(xw_scratch) % 256) return fail(RNN_ERR_ARG, cell, "xw_scratch: not 256-byte aligned");
+  }
+  if (!state_scratch) return fail(RNN_ERR_ARG, cell, "state_scratch: NULL (needs %zu bytes)", p.st.total);
+  if (reinterpret_cast<uintptr_t>(state_scratch) % 256)
+    return fail(RNN_ERR_ARG, cell, "state_scratch: not 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* st = static_cast<char*>(state_scratch);
+  float* slab = reinterpret_cast<float*>(st + p.st.slab);
+  float* cstate = reinterpret_cast<float*>(st + p.st.cell);
+  const bool pers = p.engine == RNN_ENGINE_PERSISTENT && p.S > 0 && p.steps > 0;
+
+  // -- state setup (slot 0 of the state, the cell state, the exchange words)
+  SetupArgs sa{};
+  sa.D = p.D;
+  sa.B = int(p.B);
+  sa.H = int(p.H);
+  sa.layout = p.desc.layout;
+  sa.dtype = p.desc.dtype;
+  sa.init_h = ih;
+  sa.init_c = ic;
+  sa.slab = slab;
+  sa.cell_state = cstate;
+  sa.xch = pers ? reinterpret_cast<unsigned long long*>(st + p.st.xch) : nullptr;
+
+  StepArgs a{};
+  a.cell = cell;
+  a.G = p.G;
+  a.D = p.D;
+  a.H = int(p.H);
+  a.B = int(p.B);
+  a.S = int(p.S);
+  a.steps = int(p.steps);
+  a.dir_reverse[0] = p.desc.direction == RNN_DIR_REVERSE;
+  a.dir_reverse[1] = 1;
+  a.dtype = p.desc.dtype;
+  a.R = R;
+  a.bias = Bp;
+  a.P = P;
+  a.lens = reinterpret_cast<const int32_t*>(lens);
+  a.xw = static_cast<const float*>(xw_scratch);
+  a.slab = slab;
+  a.cell_state = cstate;
+  a.zbuf = reinterpret_cast<float*>(st + p.st.zbuf);
+  a.rhbuf = reinterpret_cast<float*>(st + p.st.rhbuf);
+  a.xch = reinterpret_cast<unsigned long long*>(st + p.st.xch);
+  a.xch2 = reinterpret_cast<unsigned long long*>(st + p.st.xch2);
+  a.clip = p.desc.clip > 0.f ? p.desc.clip : 0.f;
+  a.input_forget = p.desc.input_forget;
+  a.lbr = p.desc.linear_before_reset;
+  a.slots = p.slots;
+  for (int i = 0; i < p.slots * p.D; ++i)
+    a.act[i] = Act{p.desc.activations[i].kind, p.desc.activations[i].alpha, p.desc.activations[i].beta};
+
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
+  // 1. input projection
+  if (p.S > 0) {
+    ProjArgs pa{};
+    pa.X = X;
+    pa.W = W;
+    pa.xw = static_cast<float*>(xw_scratch);
+    pa.M = p.S * p.B;
+    pa.N = p.G * p.H;
+    pa.K = p.I;
+    pa.S = p.S;
+    pa.B = p.B;
+    pa.layout = p.desc.layout;
+    pa.D = p.D;
+    pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
+    pa.H = p.H;
+    if ((e = launch_projection(pa, p.desc.dtype, s)) != hipSuccess)
+      return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));
+  }
+  if ((e = mark(1)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
+  // 2. state setup
+  if ((e = launch_setup(sa, s)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "setup launch: %s", hipGetErrorString(e));
+  if ((e = mark(2)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
+  // 3. recurrent steps
+  if (p.S > 0 && p.steps > 0) {
+    if (pers) {
+      if ((e = launch_step_persistent(a, p, s)) != hipSuccess)
+        return fail(RNN_ERR_HIP, cell, "persistent step launch: %s", hipGetErrorString(e));
+    } else {
+      for (int step = 0; step < int(p.steps); ++step)
+        if ((e = launch_step_generic(a, step, s)) != hipSuccess)
+          return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));
+    }
+  }
+  if ((e = mark(3)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
+  // 4. outputs
+  if (Y || Yh || Yc) {
+    OutputArgs oa{};
+    oa.D = p.D;
+    oa.B = int(p.B);
+    oa.H = int(p.H);
+    oa.S = int(p.S);
+    oa.steps = int(p.steps);
+    oa.layout = p.desc.layout;
+    oa.dtype = p.desc.dtype;
+    oa.dir_reverse[0] = a.dir_reverse[0];
+    oa.dir_reverse[1] = a.dir_reverse[1];
+    oa.lens = a.lens;
+    oa.slab = slab;
+    oa.cell_state = cstate;
+    oa.Y = const_cast<char*>(Y);
+    oa.Y_h = const_cast<char*>(Yh);
+    oa.Y_c = const_cast<char*>(Yc);
+    if ((e = launch_output(oa, s)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "output launch: %s", hipGetErrorString(e));
+  }
+  if ((e = mark(4)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
+  return RNN_OK;
+}
+
+}  // namespace

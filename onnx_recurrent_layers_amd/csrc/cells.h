@@ -1,0 +1,59 @@
+// cells.h -- the gate arithmetic of one hidden unit for one batch row, in the
+// order the "Recurrent layers" page fixes ("Arithmetic and determinism"):
+// pre = ((xw + rec) + Wb) + Rb, then the peephole terms (i and f with the
+// previous cell state, o with the new one), then clip, then the activation,
+// then c = f*c + i*c~, h = o*h_act(c); GRU h = (1 - z)*h~ + z*h.  input_forget
+// and linear_before_reset follow the page's "Semantics" list.  Internal.
+#pragma once
+
+#include "device_common.h"
+
+namespace rnnhip {
+
+// pre-activation sum in the page's order; absent biases add nothing.
+__device__ __forceinline__ float pre_sum(float xw, float rec, float wb, float rb) {
+  return ((xw + rec) + wb) + rb;
+}
+
+// LSTM.  pre[g] for g = i, o, f, c (already summed); peep = P_i, P_o, P_f or
+// null; acts = f, g, h slots of this direction.
+__device__ __forceinline__ void lstm_unit(const float pre[4], const float* peep, float c_prev, float clip,
+                                          int input_forget, const Act* acts, float* h_out, float* c_out) {
+  float pi = pre[0], pf = pre[2], pc = pre[3];
+  if (peep) {
+    pi = pi + peep[0] * c_prev;
+    pf = pf + peep[2] * c_prev;
+  }
+  pi = clipf(pi, clip);
+  pf = clipf(pf, clip);
+  pc = clipf(pc, clip);
+  const float ig = activate(acts[0], pi);
+  const float fg = input_forget ? 1.f - ig : activate(acts[0], pf);
+  const float ct = activate(acts[1], pc);
+  const float c = fg * c_prev + ig * ct;
+  float po = pre[1];
+  if (peep) po = po + peep[1] * c;
+  po = clipf(po, clip);
+  const float og = activate(acts[0], po);
+  *c_out = c;
+  *h_out = og * activate(acts[2], c);
+}
+
+// GRU update-gate and reset-gate activations.
+__device__ __forceinline__ float gru_gate(float pre, float clip, const Act* acts) {
+  return activate(acts[0], clipf(pre, clip));
+}
+
+// GRU candidate and new state.  `ph` is the candidate pre-activation already
+// formed in the right order for linear_before_reset (see the step kernels).
+__device__ __forceinline__ float gru_unit(float z, float ph, float h_prev, float clip, const Act* acts) {
+  const float hh = activate(acts[1], clipf(ph, clip));
+  return (1.f - z) * hh + z * h_prev;
+}
+
+// Plain RNN.
+__device__ __forceinline__ float rnn_unit(float pre, float clip, const Act* acts) {
+  return activate(acts[0], clipf(pre, clip));
+}
+
+}  // namespace rnnhip

@@ -1,0 +1,70 @@
+// device_common.h -- device helpers shared by the kernels: element loads,
+// f16 rounding, the ONNX activations and clip.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "plan.h"
+
+namespace rnnhip {
+
+typedef _Float16 half_t;
+
+// Widen one stored element (f32, or f16 which widens exactly) to f32.
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i) {
+  return static_cast<float>(p[i]);
+}
+
+// Round an f32 value to the tensor type: f16 rounds to nearest even (the
+// hardware conversion under the default round-to-nearest-even mode).
+template <typename T>
+__device__ __forceinline__ T to_elem(float v) {
+  return static_cast<T>(v);
+}
+
+// clip: clamp to [-c, c] when c > 0.  Compare-and-select so that NaN passes
+// (fminf/fmaxf would turn it into a bound).
+__device__ __forceinline__ float clipf(float x, float c) {
+  if (c > 0.f) {
+    x = x < -c ? -c : x;
+    x = x > c ? c : x;
+  }
+  return x;
+}
+
+// The eleven ONNX activations in f32 (alpha, beta resolved by the caller).
+__device__ __forceinline__ float activate(int kind, float a, float b, float x) {
+  switch (kind) {
+    case RNN_ACT_RELU: return x < 0.f ? 0.f : x;
+    case RNN_ACT_TANH: return tanhf(x);
+    case RNN_ACT_SIGMOID: return 1.f / (1.f + expf(-x));
+    case RNN_ACT_AFFINE: return a * x + b;
+    case RNN_ACT_LEAKY_RELU: return x >= 0.f ? x : a * x;
+    case RNN_ACT_THRESHOLDED_RELU: return x > a ? x : 0.f;
+    case RNN_ACT_SCALED_TANH: return a * tanhf(b * x);
+    case RNN_ACT_HARD_SIGMOID: {
+      float v = a * x + b;
+      v = v < 0.f ? 0.f : v;
+      return v > 1.f ? 1.f : v;
+    }
+    case RNN_ACT_ELU: return x >= 0.f ? x : a * expm1f(x);
+    case RNN_ACT_SOFTSIGN: return x / (1.f + fabsf(x));
+    case RNN_ACT_SOFTPLUS: return (x > 0.f ? x : 0.f) + log1pf(expf(-fabsf(x)));  // log(1+e^x), overflow-free
+    default: return __builtin_nanf("");
+  }
+}
+
+__device__ __forceinline__ float activate(const Act& a, float x) { return activate(a.kind, a.alpha, a.beta, x); }
+
+// Step-to-time map of one (direction, batch row): the row runs its first L
+// steps; a reverse direction starts at L-1.
+__device__ __forceinline__ int row_length(const int32_t* lens, int b, int S, int steps) {
+  int L = lens ? lens[b] : S;
+  L = L < 0 ? 0 : L;
+  L = L > S ? S : L;
+  return L < steps ? L : steps;
+}
+
+}  // namespace rnnhip

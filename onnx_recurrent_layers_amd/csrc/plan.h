@@ -1,0 +1,119 @@
+// plan.h -- the validated problem and the launch interface between the host
+// library (api.cpp) and the kernel files.  Internal; not part of the C ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/rnn.h"
+
+namespace rnnhip {
+
+constexpr int kMaxActs = 6;
+
+struct Act {
+  int32_t kind;
+  float alpha;
+  float beta;
+};
+
+// Byte offsets of the regions inside the caller's state scratch.
+struct StateLayout {
+  size_t slab;     // f32 h after every step: [steps+1][D][B][H]; slot 0 = initial h
+  size_t cell;     // f32 c: [D][B][H] (LSTM), updated in place, final after the last step
+  size_t zbuf;     // f32 GRU z for the two-phase step: [D][B][H]
+  size_t rhbuf;    // f32 GRU r*h for the two-phase step: [D][B][H]
+  size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
+  size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
+  size_t total;
+};
+
+struct Problem {
+  rnn_problem_desc desc;
+  int G = 1;        // gates
+  int D = 1;        // directions
+  int slots = 1;    // activation slots per direction
+  int64_t S = 0, B = 0, I = 0, H = 0;
+  int64_t steps = 0;  // steps run: max_length or S
+  int esize = 4;      // element size of float tensors
+  size_t xw_bytes = 0;
+  StateLayout st{};
+  int engine = RNN_ENGINE_LAUNCH;
+  // persistent engine geometry
+  int pers_blocks = 0;       // workgroups of the cooperative launch
+  int pers_units = 0;        // units per workgroup
+  int pers_wg_per_dir = 0;
+};
+
+// Arguments shared by the step kernels.
+struct StepArgs {
+  int cell, G, D, H, B, S;
+  int steps;
+  int dir_reverse[2];      // 1 when direction d runs backwards in time
+  int dtype;               // RNN_DTYPE_*
+  const void* R;           // [D][G*H][H]
+  const void* bias;        // [D][2*G*H] or null
+  const void* P;           // [D][3*H] or null
+  const int32_t* lens;     // [B] or null
+  const float* xw;         // [D][S][B][G*H]
+  float* slab;             // [steps+1][D][B][H]
+  float* cell_state;       // [D][B][H]
+  float* zbuf;             // [D][B][H]
+  float* rhbuf;            // [D][B][H]
+  unsigned long long* xch; // [2][D][B][H]
+  unsigned long long* xch2;// [2][D][B][H]
+  float clip;              // > 0: clamp
+  int input_forget;
+  int lbr;
+  int slots;
+  Act act[kMaxActs];
+};
+
+struct ProjArgs {
+  const void* X;      // layout-mapped rows
+  const void* W;      // [D][N][K]
+  float* xw;          // [D][M][N], M = S*B (row t*B+b)
+  int64_t M, N, K;
+  int64_t S, B;
+  int layout;
+  int D;
+  int skip_block;     // gate block of H columns not needed (input_forget: f), or -1
+  int64_t H;
+};
+
+struct SetupArgs {
+  int D, B, H;
+  int layout;
+  int dtype;
+  const void* init_h;  // or null
+  const void* init_c;  // or null
+  float* slab;         // slot 0
+  float* cell_state;
+  unsigned long long* xch;   // or null (no persistent engine)
+};
+
+struct OutputArgs {
+  int D, B, H, S;
+  int steps;
+  int layout;
+  int dtype;
+  int dir_reverse[2];
+  const int32_t* lens;
+  const float* slab;
+  const float* cell_state;
+  void* Y;     // or null
+  void* Y_h;   // or null
+  void* Y_c;   // or null
+};
+
+hipError_t launch_projection(const ProjArgs& a, int dtype, hipStream_t s);
+hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
+hipError_t launch_output(const OutputArgs& a, hipStream_t s);
+hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
+int step_generic_launches_per_step(const StepArgs& a);
+hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, hipStream_t s);
+bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per_dir);
+
+}  // namespace rnnhip

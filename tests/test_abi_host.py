@@ -1,0 +1,193 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads and exports every function rnn.h declares; descriptions and
+operands are validated before anything is enqueued, with messages that name
+the cell and the argument; scratch sizes and the launch plan."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import onnx_recurrent_layers_amd as rl
+from onnx_recurrent_layers_amd.synth import LayerSpec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rl.LIB_PATH):
+        from onnx_recurrent_layers_amd import build
+        build.build(verbose=False)
+    return rl.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rnn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(rnn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(lib, n), f"library does not export {n}"
+
+
+def spec(cell="LSTM", **kw):
+    base = dict(seq=5, batch=3, input=4, hidden=6)
+    base.update(kw)
+    return LayerSpec(cell, **base)
+
+
+def create_err(desc):
+    h = ctypes.c_void_p(1234)
+    rc = rl.load_library().rnn_problem_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, rl.rnn_last_error(), h.value
+
+
+@pytest.mark.parametrize("cell,field,value,code,needle", [
+    ("LSTM", "seq", -1, rl.RNN_ERR_SHAPE, "seq"),
+    ("GRU", "batch", -2, rl.RNN_ERR_SHAPE, "batch"),
+    ("RNN", "input", -1, rl.RNN_ERR_SHAPE, "input"),
+    ("LSTM", "hidden", 0, rl.RNN_ERR_SHAPE, "hidden"),
+    ("GRU", "layout", 2, rl.RNN_ERR_ARG, "layout"),
+    ("RNN", "direction", 3, rl.RNN_ERR_ARG, "direction"),
+    ("LSTM", "dtype", 7, rl.RNN_ERR_ARG, "dtype"),
+    ("GRU", "input_forget", 1, rl.RNN_ERR_ARG, "only an LSTM takes input_forget"),
+    ("RNN", "input_forget", 1, rl.RNN_ERR_ARG, "only an LSTM takes input_forget"),
+    ("LSTM", "linear_before_reset", 1, rl.RNN_ERR_ARG, "only a GRU takes linear_before_reset"),
+    ("RNN", "linear_before_reset", 1, rl.RNN_ERR_ARG, "only a GRU takes linear_before_reset"),
+    ("LSTM", "input_forget", 2, rl.RNN_ERR_ARG, "input_forget"),
+    ("GRU", "max_length", 6, rl.RNN_ERR_SHAPE, "max_length"),
+    ("GRU", "max_length", -1, rl.RNN_ERR_SHAPE, "max_length"),
+    ("LSTM", "num_activations", 2, rl.RNN_ERR_ARG, "activations"),
+    ("LSTM", "clip", float("nan"), rl.RNN_ERR_ARG, "clip"),
+    ("RNN", "engine", 9, rl.RNN_ERR_ARG, "engine"),
+])
+def test_create_rejects(lib, cell, field, value, code, needle):
+    d = rl.make_desc(spec(cell))
+    setattr(d, field, value)
+    rc, msg, h = create_err(d)
+    assert rc == code, (rc, msg)
+    assert needle in msg and msg.startswith(cell), msg
+    assert h is None
+
+
+def test_bad_activation_kind(lib):
+    d = rl.make_desc(spec("GRU", direction="bidirectional"))
+    d.activations[3].kind = 11
+    rc, msg, _ = create_err(d)
+    assert rc == rl.RNN_ERR_ARG and "activations[3]" in msg and msg.startswith("GRU")
+
+
+def test_size_overflow_is_shape_error(lib):
+    d = rl.make_desc(spec("LSTM"))
+    d.seq, d.batch, d.input = 1 << 29, 1 << 29, 1 << 20
+    rc, msg, _ = create_err(d)
+    assert rc == rl.RNN_ERR_SHAPE and "overflow" in msg
+
+
+@pytest.mark.parametrize("cell,direction,G", [("LSTM", "bidirectional", 4), ("GRU", "forward", 3), ("RNN", "reverse", 1)])
+def test_scratch_sizes(lib, cell, direction, G):
+    s = spec(cell, direction=direction, seq=7, batch=3, hidden=5)
+    h = rl.rnn_problem_create(rl.make_desc(s, "launch"))
+    xw, st = rl.rnn_scratch_size(h)
+    D = 2 if direction == "bidirectional" else 1
+    assert xw == 4 * D * 7 * 3 * G * 5
+    assert st >= 4 * (7 + 1) * D * 3 * 5
+    assert st % 256 == 0
+    rl.rnn_problem_destroy(h)
+
+
+def test_empty_batch_and_seq_sizes(lib):
+    h = rl.rnn_problem_create(rl.make_desc(spec("LSTM", batch=0)))
+    assert rl.rnn_scratch_size(h) == (0, 0)
+    assert rl.rnn_problem_plan(h).launches == 0
+    rl.rnn_problem_destroy(h)
+    h = rl.rnn_problem_create(rl.make_desc(spec("LSTM", seq=0)))
+    xw, st = rl.rnn_scratch_size(h)
+    assert xw == 0 and st > 0
+    assert rl.rnn_problem_plan(h).launches == 2   # setup + outputs
+    rl.rnn_problem_destroy(h)
+
+
+@pytest.mark.parametrize("cell,lbr,per_step", [("LSTM", 0, 1), ("GRU", 1, 1), ("GRU", 0, 2), ("RNN", 0, 1)])
+def test_launch_plan_one_pass_per_step(lib, cell, lbr, per_step):
+    s = spec(cell, seq=9, linear_before_reset=lbr, max_length=6)
+    h = rl.rnn_problem_create(rl.make_desc(s, "launch"))
+    info = rl.rnn_problem_plan(h)
+    assert info.engine == rl.ENGINES["launch"] and info.steps == 6
+    assert info.launches == 1 + 1 + 6 * per_step + 1
+    rl.rnn_problem_destroy(h)
+
+
+class FakeTensor:
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def encode_err(s, tensors, offsets=None, xw=4096, state=4096):
+    h = rl.rnn_problem_create(rl.make_desc(s, "launch"))
+    ops = rl.make_operands(tensors, offsets)
+    rc = rl.load_library().rnn_encode(h, ctypes.byref(ops), ctypes.c_void_p(xw), ctypes.c_void_p(state), None)
+    msg = rl.rnn_last_error()
+    rl.rnn_problem_destroy(h)
+    return rc, msg
+
+
+BASE = {"X": FakeTensor(1 << 20), "W": FakeTensor(2 << 20), "R": FakeTensor(3 << 20)}
+
+
+@pytest.mark.parametrize("cell,extra,code,needle", [
+    ("GRU", {"initial_c": FakeTensor(4 << 20)}, rl.RNN_ERR_ARG, "only an LSTM takes initial_c"),
+    ("RNN", {"P": FakeTensor(4 << 20)}, rl.RNN_ERR_ARG, "only an LSTM takes peepholes"),
+    ("GRU", {"Y_c": FakeTensor(4 << 20)}, rl.RNN_ERR_ARG, "only an LSTM has Y_c"),
+    ("LSTM", {"X": None}, rl.RNN_ERR_ARG, "X: NULL"),
+    ("LSTM", {"W": None}, rl.RNN_ERR_ARG, "W: NULL"),
+    ("GRU", {"R": None}, rl.RNN_ERR_ARG, "R: NULL"),
+])
+def test_encode_rejects_operands(lib, cell, extra, code, needle):
+    t = dict(BASE)
+    t.update(extra)
+    t = {k: v for k, v in t.items() if v is not None}
+    rc, msg = encode_err(spec(cell), t)
+    assert rc == code and needle in msg and msg.startswith(cell), msg
+
+
+def test_encode_rejects_misaligned_and_negative_offsets(lib):
+    rc, msg = encode_err(spec("LSTM", dtype="f32"), dict(BASE, Y=FakeTensor((5 << 20) + 2)))
+    assert rc == rl.RNN_ERR_ARG and "Y: address not aligned" in msg
+    rc, msg = encode_err(spec("GRU", dtype="f16"), BASE, offsets={"R": -1})
+    assert rc == rl.RNN_ERR_ARG and "R: negative element offset" in msg
+    # odd element offsets of f16 tensors are fine for validation
+    rc, msg = encode_err(spec("GRU", dtype="f16", batch=0), BASE, offsets={"X": 3, "W": 5})
+    assert rc == rl.RNN_OK, msg
+
+
+def test_encode_rejects_missing_or_misaligned_scratch(lib):
+    rc, msg = encode_err(spec("LSTM"), BASE, xw=0)
+    assert rc == rl.RNN_ERR_ARG and "xw_scratch" in msg
+    rc, msg = encode_err(spec("LSTM"), BASE, state=0)
+    assert rc == rl.RNN_ERR_ARG and "state_scratch" in msg
+    rc, msg = encode_err(spec("LSTM"), BASE, state=4096 + 64)
+    assert rc == rl.RNN_ERR_ARG and "256-byte" in msg
+
+
+def test_batch_zero_records_nothing(lib):
+    rc, msg = encode_err(spec("RNN", batch=0), BASE, xw=0, state=0)
+    assert rc == rl.RNN_OK, msg
+
+
+def test_validate_lengths(lib):
+    assert rl.rnn_validate_lengths(np.array([3, 0, 5, 2]), 5) == 5
+    with pytest.raises(rl.RnnError) as e:
+        rl.rnn_validate_lengths(np.array([3, 6]), 5)
+    assert e.value.code == rl.RNN_ERR_SHAPE and "sequence_lens[1]" in e.value.message
+    with pytest.raises(rl.RnnError):
+        rl.rnn_validate_lengths(np.array([-1]), 5)

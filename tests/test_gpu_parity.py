@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Bar: max abs error 1e-4 for f32 outputs and 5e-3 for f16 outputs; two runs
+bit-identical; nothing outside an output's extent written (sentinels)."""
+import itertools
+
+import numpy as np
+import pytest
+
+from onnx_recurrent_layers_amd import synth
+from onnx_recurrent_layers_amd.synth import LayerSpec, Dists, make_inputs
+from oracle import oracle
+from tests.gpu_harness import gpu_layer, compare, oracle_rows, select_rows, note
+
+pytestmark = pytest.mark.gpu
+
+ENGINES = ["launch"]
+
+
+def check(spec, inputs, engine="auto", offsets=None, twice=True, what=""):
+    note(f"case {what} engine={engine} spec={spec}")
+    got = gpu_layer(spec, inputs, engine=engine, offsets=offsets)
+    ref = oracle.run(spec, inputs, outputs=spec.outputs)
+    rep = compare(spec, got, ref, what=what)
+    if twice:
+        again = gpu_layer(spec, inputs, engine=engine, offsets=offsets)
+        for n in got:
+            assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), f"{what} {n}: runs differ"
+    return rep
+
+
+# ---------------------------------------------------------------------------
+# projection (stage 1) against the oracle's plain product, read from scratch
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,layout", [("f32", 0), ("f16", 0), ("f32", 1), ("f16", 1)])
+def test_projection_scratch(dtype, layout):
+    import torch
+    spec = LayerSpec("LSTM", seq=13, batch=11, input=70, hidden=37, layout=layout, dtype=dtype,
+                     direction="bidirectional", outputs=("Y_h",))
+    inp = make_inputs(spec, 5)
+    note(f"case projection {dtype} L{layout}")
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    D, S, B, G, H, I = 2, spec.seq, spec.batch, 4, spec.hidden, spec.input
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
+    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
+    A = X.reshape(S * B, I)
+    for d in range(D):
+        ref = oracle.projection(A, inp["W"][d])
+        err = np.max(np.abs(xw[d].astype(np.float64) - ref))
+        assert err <= 1e-4, (d, err)
+
+
+# ---------------------------------------------------------------------------
+# the page's test matrix on small shapes that span several tiles and a ragged tail
+# ---------------------------------------------------------------------------
+MATRIX = []
+for cell, direction, layout, dtype in itertools.product(("LSTM", "GRU", "RNN"),
+                                                         ("forward", "reverse", "bidirectional"),
+                                                         (0, 1), ("f32", "f16")):
+    MATRIX.append((cell, direction, layout, dtype))
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("cell,direction,layout,dtype", MATRIX, ids=["-".join(map(str, m)) for m in MATRIX])
+def test_matrix_options(cell, direction, layout, dtype, engine):
+    lbrs = (0, 1) if cell == "GRU" else (0,)
+    for lbr in lbrs:
+        spec = LayerSpec(cell, seq=9, batch=11, input=70, hidden=37, direction=direction, layout=layout,
+                         dtype=dtype, linear_before_reset=lbr, init_h=True, init_c=cell == "LSTM",
+                         lens=True, peephole=cell == "LSTM", clip=2.5,
+                         outputs=("Y", "Y_h", "Y_c"))
+        inp = make_inputs(spec, 17, Dists(sequence_lens=("I", 0, 9), W=("U", -0.3, 0.3), R=("U", -0.3, 0.3)))
+        check(spec, inp, engine=engine, what=f"{cell}/{direction}/L{layout}/{dtype}/lbr{lbr}")
+    if cell == "LSTM":
+        spec = LayerSpec(cell, seq=6, batch=9, input=33, hidden=70, direction=direction, layout=layout,
+                         dtype=dtype, input_forget=1, peephole=True, bias=False, lens=False)
+        check(spec, make_inputs(spec, 18), engine=engine, what=f"LSTM input_forget {direction} L{layout} {dtype}")
+
+
+ALL_ACTS = [("Relu", 0, 0), ("Tanh", 0, 0), ("Sigmoid", 0, 0), ("Affine", 0.7, -0.2), ("LeakyRelu", 0.03, 0),
+            ("ThresholdedRelu", 0.2, 0), ("ScaledTanh", 1.5, 0.5), ("HardSigmoid", 0.2, 0.5), ("Elu", 0.8, 0),
+            ("Softsign", 0, 0), ("Softplus", 0, 0)]
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("cell", ["LSTM", "GRU", "RNN"])
+def test_every_activation_in_every_slot(cell, engine):
+    slots = synth.SLOTS[cell]
+    for i, act in enumerate(ALL_ACTS):
+        for slot in range(2 * slots):
+            acts = list(synth.DEFAULT_ACTS[cell]) * 2
+            acts[slot] = act
+            acts[(slot + 3) % (2 * slots)] = ALL_ACTS[(i + 5) % len(ALL_ACTS)]
+            spec = LayerSpec(cell, seq=4, batch=3, input=5, hidden=19, direction="bidirectional", acts=acts,
+                             init_h=True, dtype="f32" if (i + slot) % 2 == 0 else "f16",
+                             linear_before_reset=slot % 2 if cell == "GRU" else 0)
+            check(spec, make_inputs(spec, 100 + i), engine=engine, twice=False,
+                  what=f"{cell} act {act[0]} slot {slot}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_odd_offsets_with_sentinels(dtype, engine):
+    offs = {n: 3 for n in ("X", "W", "R", "B", "sequence_lens", "initial_h", "initial_c", "P", "Y", "Y_h", "Y_c")}
+    for cell in ("LSTM", "GRU", "RNN"):
+        spec = LayerSpec(cell, seq=5, batch=3, input=7, hidden=13, direction="bidirectional", dtype=dtype,
+                         init_h=True, init_c=cell == "LSTM", peephole=cell == "LSTM", lens=True)
+        inp = make_inputs(spec, 7)
+        check(spec, inp, engine=engine, offsets={k: v for k, v in offs.items() if k in inp or k.startswith("Y")},
+              what=f"offsets {cell} {dtype}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_empty_sequence_and_batch(engine):
+    for cell in ("LSTM", "GRU", "RNN"):
+        spec = LayerSpec(cell, seq=0, batch=3, input=4, hidden=5, init_h=True, init_c=cell == "LSTM",
+                         direction="bidirectional")
+        inp = make_inputs(spec, 3)
+        got = gpu_layer(spec, inp, engine=engine)
+        ref = oracle.run(spec, inp)
+        compare(spec, got, ref, what=f"seq0 {cell}")
+        spec = LayerSpec(cell, seq=4, batch=0, input=4, hidden=5)
+        got = gpu_layer(spec, make_inputs(spec, 3), engine=engine)
+        for v in got.values():
+            assert v.size == 0
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_lengths_edge_cases_and_max_length(engine):
+    for cell in ("LSTM", "GRU", "RNN"):
+        spec = LayerSpec(cell, seq=6, batch=5, input=4, hidden=9, direction="bidirectional", init_h=True,
+                         init_c=cell == "LSTM", lens=True)
+        inp = make_inputs(spec, 9)
+        inp["sequence_lens"] = np.array([0, 6, 3, 17, -2], np.int32)  # > Seq acts as Seq; < 0 as 0
+        check(spec, inp, engine=engine, what=f"lens edges {cell}")
+        inp["sequence_lens"] = np.array([0, 4, 3, 1, 2], np.int32)
+        check(spec.replace(max_length=4), inp, engine=engine, what=f"max_length {cell}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_batch_above_eight_and_hidden_not_dividing(engine):
+    for cell, H in (("LSTM", 65), ("GRU", 127), ("RNN", 129)):
+        spec = LayerSpec(cell, seq=5, batch=19, input=31, hidden=H, direction="bidirectional", init_h=True,
+                         lens=True, linear_before_reset=0)
+        check(spec, make_inputs(spec, 21), engine=engine, what=f"B19 H{H} {cell}")
+
+
+# ---------------------------------------------------------------------------
+# the five seeded workloads at full size
+# ---------------------------------------------------------------------------
+FULL = [("C1", {}), ("C2", {}), ("C3", {"linear_before_reset": 0}), ("C3", {"linear_before_reset": 1}),
+        ("C4", {}), ("C5", {})]
+SAMPLE_ROWS = {"C4": [0, 9, 31, 63], "C5": [0, 255]}
+
+
+@pytest.mark.parametrize("name,over", FULL, ids=[f"{n}-{o}" for n, o in FULL])
+def test_full_config(name, over):
+    spec, inp = synth.config(name, **over)
+    note(f"case {name} {over} engine=auto")
+    got = gpu_layer(spec, inp, engine="auto")
+    again = gpu_layer(spec, inp, engine="auto")
+    for n in got:
+        assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), f"{name} {n}: runs differ"
+    rows = SAMPLE_ROWS.get(name)
+    if rows is None:
+        ref = oracle.run(spec, inp, outputs=spec.outputs)
+        rep = compare(spec, got, ref, what=name)
+    else:
+        ref = oracle_rows(spec, inp, rows, outputs=spec.outputs)
+        rep = compare(spec, select_rows(spec, got, rows), ref, what=name)
+    note(f"{name} {over}: " + ", ".join(f"{k} abs {v[0]:.3g} scaled {v[1]:.3g}" for k, v in rep.items()))
