@@ -34,7 +34,8 @@ class HipEvents:
     """hipEvent_t handles through the HIP runtime's C API."""
 
     def __init__(self, n: int):
-        self.hip = ctypes.CDLL("libamdhip64.so")
+        import onnx_recurrent_layers_amd as rl
+        self.hip = rl.hip_runtime()
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -129,7 +130,7 @@ def main() -> int:
     value = n_steps / (ms_per_step / 1000.0)
 
     # roofline of the recurrent-step kernel (dominant): algorithmic bytes per launch / launch time
-    step_launches = max(1, plan.launches - 3)           # minus projection, setup, output
+    step_launches = max(1, plan.step_launches)
     steps_per_launch = n_steps / step_launches
     launch_ms = med["steps"] / step_launches
     bytes_per_launch = step_bytes(spec) * steps_per_launch

@@ -166,7 +166,8 @@ typedef struct {
   int32_t engine;          /* rnn_engine actually used */
   int32_t steps;           /* number of recurrent steps run (max_length or S) */
   int32_t launches;        /* kernel launches per rnn_encode */
-  int32_t step_blocks;     /* workgroups of the step kernel */
+  int32_t step_blocks;     /* workgroups of the persistent step kernel (0 for the per-step engine) */
+  int32_t step_launches;   /* launches of the recurrent-step stage per rnn_encode */
 } rnn_plan_info;
 int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info);
 

@@ -61,7 +61,7 @@ class rnn_operands(ctypes.Structure):
 
 class rnn_plan_info(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("steps", ctypes.c_int32), ("launches", ctypes.c_int32),
-                ("step_blocks", ctypes.c_int32)]
+                ("step_blocks", ctypes.c_int32), ("step_launches", ctypes.c_int32)]
 
 
 _lib = None
@@ -74,6 +74,12 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m onnx_recurrent_layers_amd.build`")
+    # One HIP runtime per process: when PyTorch supplies device memory and
+    # streams, load it first so that this library binds to the same runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.rnn_problem_create.argtypes = [P(rnn_problem_desc), P(ctypes.c_void_p)]
@@ -95,6 +101,16 @@ def load_library(path: str = LIB_PATH):
     lib.rnn_last_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def hip_runtime():
+    """The HIP runtime library this process uses (the one the library is bound to)."""
+    load_library()
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if os.path.basename(path).startswith("libamdhip64.so"):
+            return ctypes.CDLL(path)
+    return ctypes.CDLL("libamdhip64.so")
 
 
 def rnn_last_error() -> str:

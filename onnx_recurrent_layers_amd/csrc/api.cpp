@@ -144,29 +144,31 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   int64_t slab;
   if (!mul_ok(p->steps + 1, dbh, &slab) || !mul_ok(slab, 4, &slab) || slab > kMaxBytes)
     return bad(RNN_ERR_SHAPE, "state scratch: size overflows");
-  StateLayout& st = p->st;
-  size_t off = 0;
-  st.slab = off;  off = align256(off + size_t(slab));
-  st.cell = off;  off = align256(off + size_t(dbh) * 4);
-  st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
-  st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
-
   // Engine choice.
   int blocks = 0, units = 0, wpd = 0;
   const bool pers_ok = persistent_supported(*p, &blocks, &units, &wpd);
   int engine = desc->engine;
+  if (p->S == 0 || p->steps == 0 || p->B == 0) engine = RNN_ENGINE_LAUNCH;  // nothing to step
   if (engine == RNN_ENGINE_AUTO) engine = pers_ok ? RNN_ENGINE_PERSISTENT : RNN_ENGINE_LAUNCH;
   if (engine == RNN_ENGINE_PERSISTENT && !pers_ok)
     return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
   p->engine = engine;
+
+  StateLayout& st = p->st;
+  st = StateLayout{};
+  size_t off = 0;
   if (engine == RNN_ENGINE_PERSISTENT) {
     p->pers_blocks = blocks;
     p->pers_units = units;
     p->pers_wg_per_dir = wpd;
-    st.xch = off;  off = align256(off + 2 * size_t(dbh) * 8);
-    st.xch2 = off; off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
+    st.xch = off;   off = align256(off + 2 * size_t(dbh) * 8);
+    st.xch2 = off;  off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
+    st.status = off; off = align256(off + 4);
   } else {
-    st.xch = st.xch2 = off;
+    st.slab = off;  off = align256(off + size_t(slab));
+    st.cell = off;  off = align256(off + size_t(dbh) * 4);
+    st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+    st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
   }
   st.total = p->B > 0 ? off : 0;
 
@@ -222,9 +224,10 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
     if (p->S > 0) n += 1;          // projection
     n += 1;                        // state setup
     if (p->S > 0) n += step_launch_count(*p);
-    n += 1;                        // outputs (one kernel covers Y, Y_h, Y_c)
+    if (p->engine != RNN_ENGINE_PERSISTENT) n += 1;  // output pass (the persistent engine writes outputs itself)
   }
   info->launches = n;
+  info->step_launches = (p->B > 0 && p->S > 0) ? step_launch_count(*p) : 0;
   return RNN_OK;
 }
 
@@ -305,9 +308,10 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* st = static_cast<char*>(state_scratch);
-  float* slab = reinterpret_cast<float*>(st + p.st.slab);
-  float* cstate = reinterpret_cast<float*>(st + p.st.cell);
-  const bool pers = p.engine == RNN_ENGINE_PERSISTENT && p.S > 0 && p.steps > 0;
+  const bool pers = p.engine == RNN_ENGINE_PERSISTENT;
+  float* slab = pers ? nullptr : reinterpret_cast<float*>(st + p.st.slab);
+  float* cstate = pers ? nullptr : reinterpret_cast<float*>(st + p.st.cell);
+  int* status = pers ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
 
   // -- state setup (slot 0 of the state, the cell state, the exchange words)
   SetupArgs sa{};
@@ -321,6 +325,9 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.slab = slab;
   sa.cell_state = cstate;
   sa.xch = pers ? reinterpret_cast<unsigned long long*>(st + p.st.xch) : nullptr;
+  sa.xch2 = (pers && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
+                ? reinterpret_cast<unsigned long long*>(st + p.st.xch2) : nullptr;
+  sa.status = status;
 
   StepArgs a{};
   a.cell = cell;
@@ -382,7 +389,8 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   // 3. recurrent steps
   if (p.S > 0 && p.steps > 0) {
     if (pers) {
-      if ((e = launch_step_persistent(a, p, s)) != hipSuccess)
+      PersistentIO io{ih, ic, const_cast<char*>(Y), const_cast<char*>(Yh), const_cast<char*>(Yc), status};
+      if ((e = launch_step_persistent(a, p, io, s)) != hipSuccess)
         return fail(RNN_ERR_HIP, cell, "persistent step launch: %s", hipGetErrorString(e));
     } else {
       for (int step = 0; step < int(p.steps); ++step)
@@ -391,8 +399,8 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     }
   }
   if ((e = mark(3)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
-  // 4. outputs
-  if (Y || Yh || Yc) {
+  // 4. outputs (the persistent engine writes them itself)
+  if (!pers && (Y || Yh || Yc)) {
     OutputArgs oa{};
     oa.D = p.D;
     oa.B = int(p.B);

@@ -34,16 +34,27 @@ __device__ __forceinline__ float clipf(float x, float c) {
   return x;
 }
 
+// Logistic sigmoid 1/(1+e^-x) from the hardware exponential (v_exp_f32) and
+// reciprocal; relative error a few ulp, saturating to 0 and 1, NaN passes.
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+// tanh(x) = 1 - 2/(e^(2x)+1): absolute error a few 1e-8, exact limits +-1, NaN passes.
+__device__ __forceinline__ float tanh_f(float x) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * x) + 1.f);
+}
+
 // The eleven ONNX activations in f32 (alpha, beta resolved by the caller).
 __device__ __forceinline__ float activate(int kind, float a, float b, float x) {
   switch (kind) {
     case RNN_ACT_RELU: return x < 0.f ? 0.f : x;
-    case RNN_ACT_TANH: return tanhf(x);
-    case RNN_ACT_SIGMOID: return 1.f / (1.f + expf(-x));
+    case RNN_ACT_TANH: return tanh_f(x);
+    case RNN_ACT_SIGMOID: return sigmoid_f(x);
     case RNN_ACT_AFFINE: return a * x + b;
     case RNN_ACT_LEAKY_RELU: return x >= 0.f ? x : a * x;
     case RNN_ACT_THRESHOLDED_RELU: return x > a ? x : 0.f;
-    case RNN_ACT_SCALED_TANH: return a * tanhf(b * x);
+    case RNN_ACT_SCALED_TANH: return a * tanh_f(b * x);
     case RNN_ACT_HARD_SIGMOID: {
       float v = a * x + b;
       v = v < 0.f ? 0.f : v;

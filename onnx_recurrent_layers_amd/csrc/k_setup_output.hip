@@ -20,14 +20,19 @@ __global__ void setup_kernel(SetupArgs a) {
     const int64_t src = a.layout == 0 ? i : (b * a.D + d) * a.H + j;
     const float h0 = a.init_h ? ld(static_cast<const T*>(a.init_h), src) : 0.f;
     const float c0 = a.init_c ? ld(static_cast<const T*>(a.init_c), src) : 0.f;
-    a.slab[i] = h0;
-    a.cell_state[i] = c0;
+    if (a.slab) a.slab[i] = h0;
+    if (a.cell_state) a.cell_state[i] = c0;
     if (a.xch) {
       // word = (tag << 32) | value bits; slot 0 carries step 0, slot 1 no step yet.
       a.xch[i] = (0ull << 32) | __float_as_uint(h0);
       a.xch[DBH + i] = 0xffffffffull << 32;
     }
+    if (a.xch2) {
+      a.xch2[i] = 0xffffffffull << 32;
+      a.xch2[DBH + i] = 0xffffffffull << 32;
+    }
   }
+  if (a.status && blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
 }
 
 template <typename T>

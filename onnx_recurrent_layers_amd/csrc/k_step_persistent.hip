@@ -1,10 +1,536 @@
-// k_step_persistent.hip -- stage 3 as one cooperative launch (placeholder).
+// k_step_persistent.hip -- stage 3 of a layer ("Recurrent layers" page, "How a
+// layer runs", item 3) for small batches as ONE cooperative launch that walks
+// every step, followed directly by the page's output rules ("Semantics").
+//
+// Why not a pass per step: the page avoids a grid-wide dependency because its
+// APIs cannot guarantee co-resident workgroups ("Why a pass per step").  HIP's
+// cooperative launch does guarantee it, so here each workgroup keeps its share
+// of R resident in LDS for the whole layer and the steps are ordered by
+// per-value handshakes instead of kernel boundaries.  The page's own
+// one-workgroup-per-direction attempt lost because every step's R went
+// through one compute unit; here R is spread over up to 256 compute units.
+//
+// Exchange: the hidden state of step s travels as 64-bit words
+// (tag = step << 32 | f32 bits) stored and loaded with agent-scope relaxed
+// atomics.  A reader spins until the word carries the tag it expects, so each
+// value carries its own validity: no barrier, no fence, no counter.  Two slots
+// (parity of the step) suffice: a workgroup can only overwrite a slot after
+// every workgroup of its direction has published the next step, which each of
+// them does only after it finished reading that slot.  The state setup that
+// precedes this kernel on the stream writes step 0's words and invalidates the
+// other slot, so words left by an earlier call are never taken for new ones.
+//
+// Determinism: each dot product is summed by fixed lanes in a fixed order and
+// combined by a fixed xor butterfly; nothing depends on timing.
+#include <algorithm>
+#include <cstdlib>
+
 #include "cells.h"
 
 namespace rnnhip {
 
-bool persistent_supported(const Problem&, int*, int*, int*) { return false; }
+constexpr int kPThreads = 256;
+constexpr int kMaxNB = 8;              // batch rows handled by this engine
+constexpr long kSpinLimit = 1l << 22;  // safety bound on one wait (several seconds); never reached normally
 
-hipError_t launch_step_persistent(const StepArgs&, const Problem&, hipStream_t) { return hipErrorNotSupported; }
+struct PersArgs {
+  StepArgs a;
+  int U;            // units per workgroup
+  int WPD;          // workgroups per direction
+  int NR;           // R rows per workgroup = Gp * U
+  int Gp;           // gate blocks computed (an LSTM with input_forget skips f)
+  int gate_of[4];   // gate block index of each computed block
+  int cand;         // GRU linear_before_reset = 0: index (in gate_of) of the candidate block, else -1
+  int layout;
+  const void* init_h;
+  const void* init_c;
+  void* Y;
+  void* Y_h;
+  void* Y_c;
+  int* status;      // set to 1 if a wait ran past the safety bound
+};
+
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+  return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+
+__device__ __forceinline__ unsigned long long load_word(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void put_word(unsigned long long* p, unsigned tag, float v) {
+  __hip_atomic_store(p, tagged(tag, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copy the words of step `tag` of every active batch row of one direction
+// (src: [B][H]) into hs[k][NB], waiting for each word to carry the tag.  A
+// thread keeps up to kChunk loads in flight and re-polls only stale words.
+// issue() sends the first loads; complete() waits.  Memory operations issued
+// between the two (output stores, the projection prefetch) are not waited for:
+// the load counter retires in order, so only earlier operations delay a wait.
+constexpr int kChunk = 24;
+constexpr int kPollThreads = kPThreads - 64;  // waves 1..3 poll; wave 0 computes gates and does the other memory traffic
+
+struct WordPoll {
+  unsigned long long v[kChunk];
+  bool want[kChunk];
+};
+
+// Where this thread's word slots of one chunk land: hs offset k*NB + b and the
+// batch row b (offset -1: no word).  Computed once; integer division by a
+// runtime H costs tens of instructions, far too much to redo every step.
+struct WordMap {
+  int off[kChunk];
+  int row[kChunk];
+};
+
+template <int NB>
+__device__ __forceinline__ void map_words(WordMap& m, int base, int H) {
+  const int n = NB * H;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    const int e = base + i * kPollThreads;
+    const int b = e / H;
+    m.off[i] = e < n ? (e - b * H) * NB + b : -1;
+    m.row[i] = b;
+  }
+}
+
+__device__ __forceinline__ void poll_issue(WordPoll& w, const WordMap& m, const unsigned long long* src, int base,
+                                           unsigned amask) {
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    w.want[i] = m.off[i] >= 0 && ((amask >> m.row[i]) & 1u);
+    if (w.want[i]) w.v[i] = load_word(src + base + i * kPollThreads);
+  }
+}
+
+// Returns non-zero when the safety bound was hit.
+__device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, const unsigned long long* src, int base,
+                                             float* hs, unsigned tag) {
+  int fail = 0;
+  for (long round = 0;; ++round) {
+    bool pending = false;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (w.want[i] && static_cast<unsigned>(w.v[i] >> 32) != tag) pending = true;
+    if (!pending) break;
+    if (round > kSpinLimit) {
+      fail = 1;
+      break;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (w.want[i] && static_cast<unsigned>(w.v[i] >> 32) != tag) w.v[i] = load_word(src + base + i * kPollThreads);
+  }
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i)
+    if (w.want[i]) hs[m.off[i]] = __uint_as_float(static_cast<unsigned>(w.v[i]));
+  return fail;
+}
+
+// Whole stage, run by the polling waves only (ptid = thread index among
+// them): the first chunk uses the precomputed map `m0`; further chunks (more
+// than kChunk words per polling thread) are mapped on the fly.
+template <int NB>
+__device__ __forceinline__ int stage_words(const unsigned long long* src, float* hs, unsigned tag, int H,
+                                           unsigned amask, const WordMap& m0, int ptid) {
+  int fail = 0;
+  WordPoll w;
+  poll_issue(w, m0, src, ptid, amask);
+  fail |= poll_complete(w, m0, src, ptid, hs, tag);
+  for (int base = ptid + kPollThreads * kChunk; base < NB * H; base += kPollThreads * kChunk) {
+    WordMap m;
+    map_words<NB>(m, base, H);
+    poll_issue(w, m, src, base, amask);
+    fail |= poll_complete(w, m, src, base, hs, tag);
+  }
+  return fail;
+}
+
+// Workgroup barrier that orders LDS only: global loads (the projection
+// prefetch) and stores (outputs, exchange words) stay in flight across it,
+// where __syncthreads would wait for every outstanding memory operation.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum over the 8 lanes of an aligned lane group with DPP moves (xor 1, xor 2,
+// then the half-row mirror); every lane of the group ends with the same total.
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// Four consecutive elements of an LDS row, widened to f32.
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const half_t* p) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 v = *reinterpret_cast<const h4*>(p);
+  return make_float4(float(v[0]), float(v[1]), float(v[2]), float(v[3]));
+}
+
+// rec[r][b] = sum_k Rl[r][k] * hs[k][b] for rows r in [r_lo, r_hi).  Groups
+// of 8 lanes own a row (two rows at a time for more loads in flight); lane c
+// of a group sums the chunks k = 4c..4c+3, 4c+32..4c+35, ... in increasing
+// order, and sum8 combines the eight partial sums in a fixed tree.  Rows and
+// hs are zero-padded to H4 (a multiple of 32), which adds exact zeros.
+template <typename T, int NB>
+__device__ __forceinline__ void products(const T* Rl, int RS, const float* hs, float* rec, int r_lo, int r_hi,
+                                         int H4) {
+  const int c = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  constexpr int kGroups = kPThreads / 8;
+  for (int r0 = r_lo + rg; r0 < r_hi; r0 += 2 * kGroups) {
+    const int r1 = r0 + kGroups;
+    const bool two = r1 < r_hi;
+    float acc0[NB], acc1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc0[b] = acc1[b] = 0.f;
+    const T* row0 = Rl + r0 * RS;
+    const T* row1 = Rl + (two ? r1 : r0) * RS;
+#pragma unroll 4
+    for (int k0 = 4 * c; k0 < H4; k0 += 32) {
+      const float4 a0 = ld4(row0 + k0);
+      const float4 a1 = ld4(row1 + k0);
+      const float* hk = hs + k0 * NB;
+      float hv[4 * NB];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const float4 v = ld4(hk + 4 * q);
+        hv[4 * q] = v.x;
+        hv[4 * q + 1] = v.y;
+        hv[4 * q + 2] = v.z;
+        hv[4 * q + 3] = v.w;
+      }
+      const float ra0[4] = {a0.x, a0.y, a0.z, a0.w};
+      const float ra1[4] = {a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc0[b] += ra0[i] * hv[i * NB + b];
+          acc1[b] += ra1[i] * hv[i * NB + b];
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v0 = sum8(acc0[b]);
+      const float v1 = sum8(acc1[b]);
+      if (c == b) {
+        rec[r0 * NB + b] = v0;
+        if (two) rec[r1 * NB + b] = v1;
+      }
+    }
+  }
+}
+
+template <typename T, int NB, bool DEF>
+__global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const StepArgs& a = p.a;
+  const int H = a.H, B = a.B, S = a.S, G = a.G;
+  const int tid = threadIdx.x;
+  const int d = blockIdx.x / p.WPD;
+  const int u0 = (blockIdx.x % p.WPD) * p.U;
+  const int Uw = min(p.U, H - u0);  // units of this workgroup (the last one may have fewer)
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  const int GH = G * H;
+  const int H4 = (H + 31) & ~31;     // rows and h padded with zeros to a multiple of 32
+  const int RS = H4 + 8;             // LDS row stride: the rows a wave reads start in different banks
+
+  T* Rl = reinterpret_cast<T*>(smem);
+  const size_t r_bytes = (size_t(p.NR) * RS * sizeof(T) + 15) & ~size_t(15);
+  float* hs = reinterpret_cast<float*>(smem + r_bytes);
+  float* rec = hs + NB * H4;
+
+  // R rows of this workgroup's units, resident for the whole layer
+  const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * GH * H;
+  for (int e = tid; e < p.NR * H4; e += kPThreads) {
+    const int r = e / H4, k = e - r * H4;
+    const int gi = r / p.U, uu = r - gi * p.U;
+    Rl[r * RS + k] = (uu < Uw && k < H) ? Rd[int64_t(p.gate_of[gi] * H + u0 + uu) * H + k] : T(0.f);
+  }
+  for (int e = NB * H + tid; e < NB * H4; e += kPThreads) hs[e] = 0.f;  // padded tail of h stays zero
+
+  int maxL = 0;
+  unsigned lens_left[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    lens_left[b] = b < B ? unsigned(row_length(a.lens, b, S, a.steps)) : 0u;
+    maxL = max(maxL, int(lens_left[b]));
+  }
+
+  // gate thread: (unit u0 + uu, batch row b)
+  const int g_uu = tid / NB, g_b = tid % NB;
+  const bool gthread = g_uu < Uw && g_b < B;
+  const int j = u0 + g_uu;
+  int L = 0;
+  float c = 0.f, hown = 0.f;
+  const Act* acts = a.act + d * a.slots;
+  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
+  float wb[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f}, peep[3] = {0.f, 0.f, 0.f};
+  const int64_t sidx = p.layout == 0 ? (dBH + int64_t(g_b) * H + j) : ((int64_t(g_b) * a.D + d) * H + j);
+  const bool rev = a.dir_reverse[d] != 0;
+  if (gthread) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (g_b == b) L = int(lens_left[b]);
+    hown = p.init_h ? ld(static_cast<const T*>(p.init_h), sidx) : 0.f;
+    c = p.init_c ? ld(static_cast<const T*>(p.init_c), sidx) : 0.f;
+    if (bias)
+      for (int g = 0; g < G; ++g) {
+        wb[g] = ld(bias, g * H + j);
+        rb[g] = ld(bias, GH + g * H + j);
+      }
+    if (a.P) {
+      const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
+      peep[0] = ld(P, j);
+      peep[1] = ld(P, H + j);
+      peep[2] = ld(P, 2 * H + j);
+    }
+    // outputs that no step writes: Y past the length, final states of an empty row
+    if (p.Y)
+      for (int t = L; t < S; ++t) {
+        const int64_t yi = p.layout == 0 ? ((int64_t(t) * a.D + d) * B + g_b) * H + j
+                                         : ((int64_t(g_b) * S + t) * a.D + d) * H + j;
+        static_cast<T*>(p.Y)[yi] = to_elem<T>(0.f);
+      }
+    if (L == 0) {
+      if (p.Y_h) static_cast<T*>(p.Y_h)[sidx] = to_elem<T>(0.f);
+      if (p.Y_c) static_cast<T*>(p.Y_c)[sidx] = to_elem<T>(0.f);
+    }
+  }
+  __shared__ int abort_flag;
+  if (tid == 0) abort_flag = 0;
+  __syncthreads();
+
+  int abort_run = 0;
+  const int nrows_main = p.cand >= 0 ? p.cand * p.U : p.NR;  // rows of the first product
+  // this thread's slice of the projection, fetched one step ahead (HBM latency
+  // is about a step long, so the loads for step s+1 are issued during step s)
+  auto fetch_xw = [&](int step, float* out) {
+    if (gthread && step < L) {
+      const int tt = rev ? L - 1 - step : step;
+      const float* xw = a.xw + ((int64_t(d) * S + tt) * B + g_b) * GH + j;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g < G && !(a.input_forget && g == 2)) out[g] = xw[g * H];
+    }
+  };
+  const bool poller = tid >= kPThreads - kPollThreads;
+  const int ptid = tid - (kPThreads - kPollThreads);
+  WordMap wmap;
+  if (poller) map_words<NB>(wmap, ptid, H);
+  float xnext[4] = {0.f, 0.f, 0.f, 0.f};
+  fetch_xw(0, xnext);
+  // output of the previous step, stored after the next step's word loads are issued
+  float y_prev = 0.f;
+  int64_t yi_prev = -1;
+  auto store_y = [&]() {
+    if (yi_prev >= 0) static_cast<T*>(p.Y)[yi_prev] = to_elem<T>(y_prev);
+    yi_prev = -1;
+  };
+  for (int s = 0; s < maxL; ++s) {
+    unsigned amask = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) amask |= (unsigned(s) < lens_left[b] ? 1u : 0u) << b;
+
+    const bool live = gthread && s < L;
+    const int t = rev ? L - 1 - s : s;
+    float xv[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) xv[g] = xnext[g];
+
+    // 1. h of step s, every unit of this direction, active rows only (polling
+    // waves); meanwhile wave 0 stores the previous output and prefetches.
+    int fail = 0;
+    if (poller) {
+      fail = stage_words<NB>(a.xch + (s & 1) * DBH + dBH, hs, unsigned(s), H, amask, wmap, ptid);
+    } else {
+      store_y();
+      fetch_xw(s + 1, xnext);
+    }
+    if (fail) abort_flag = 1;
+    lds_barrier();
+    if ((abort_run = abort_flag) != 0) break;
+
+    // 2. recurrent products of this workgroup's rows
+    products<T, NB>(Rl, RS, hs, rec, 0, nrows_main, H4);
+    lds_barrier();
+
+    // 3. gate arithmetic
+    float hnew = 0.f, z = 0.f;
+    if (live) {
+      auto pre = [&](int gi, int g) { return pre_sum(xv[g], rec[(gi * p.U + g_uu) * NB + g_b], wb[g], rb[g]); };
+      if (a.cell == RNN_CELL_LSTM) {
+        float p4[4];
+        p4[0] = pre(0, 0);
+        p4[1] = pre(1, 1);
+        if (a.input_forget) {
+          p4[2] = 0.f;
+          p4[3] = pre(2, 3);
+        } else {
+          p4[2] = pre(2, 2);
+          p4[3] = pre(3, 3);
+        }
+        lstm_unit<DEF>(p4, a.P ? peep : nullptr, c, a.clip, a.input_forget, acts, &hnew, &c);
+      } else if (a.cell == RNN_CELL_GRU) {
+        z = gru_gate<DEF>(pre(0, 0), a.clip, acts);
+        const float r = gru_gate<DEF>(pre(1, 1), a.clip, acts);
+        if (p.cand < 0) {
+          // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+          const float ph = (xv[2] + r * (rec[(2 * p.U + g_uu) * NB + g_b] + rb[2])) + wb[2];
+          hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
+        } else {
+          put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), r * hown);
+        }
+      } else {
+        hnew = rnn_unit<DEF>(pre(0, 0), a.clip, acts);
+      }
+    }
+
+    if (p.cand >= 0) {
+      // GRU, linear_before_reset = 0: the candidate needs r*h of every unit
+      if (poller && stage_words<NB>(a.xch2 + (s & 1) * DBH + dBH, hs, unsigned(s), H, amask, wmap, ptid))
+        abort_flag = 1;
+      lds_barrier();
+      if ((abort_run = abort_flag) != 0) break;
+      products<T, NB>(Rl, RS, hs, rec, p.cand * p.U, p.NR, H4);
+      lds_barrier();
+      if (live) {
+        // h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
+        const float ph = pre_sum(xv[2], rec[(p.cand * p.U + g_uu) * NB + g_b], wb[2], rb[2]);
+        hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
+      }
+    }
+
+    if (live) {
+      put_word(a.xch + ((s + 1) & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s + 1), hnew);
+      hown = hnew;
+      if (p.Y) {
+        yi_prev = p.layout == 0 ? ((int64_t(t) * a.D + d) * B + g_b) * H + j
+                                : ((int64_t(g_b) * S + t) * a.D + d) * H + j;
+        y_prev = hnew;
+      }
+      if (s == L - 1) {
+        if (p.Y_h) static_cast<T*>(p.Y_h)[sidx] = to_elem<T>(hnew);
+        if (p.Y_c) static_cast<T*>(p.Y_c)[sidx] = to_elem<T>(c);
+      }
+    }
+  }
+  if (!abort_run && p.Y) store_y();
+  if (abort_run && tid == 0) atomicExch(p.status, 1);
+}
+
+namespace {
+
+int next_pow2_nb(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+size_t lds_bytes(int NR, int H, int esize, int NB) {
+  const int H4 = (H + 31) & ~31;
+  const size_t r = (size_t(NR) * (H4 + 8) * esize + 15) & ~size_t(15);
+  return r + size_t(NB) * H4 * 4 + size_t(NR) * NB * 4;
+}
+
+// All activation slots are the cell's ONNX defaults.
+bool default_acts(const Problem& p) {
+  const int c = p.desc.cell;
+  for (int d = 0; d < p.D; ++d)
+    for (int k = 0; k < p.slots; ++k) {
+      const int kind = p.desc.activations[d * p.slots + k].kind;
+      const int want = (c == RNN_CELL_RNN) ? RNN_ACT_TANH : (k == 0 ? RNN_ACT_SIGMOID : RNN_ACT_TANH);
+      if (kind != want) return false;
+    }
+  return true;
+}
+
+constexpr size_t kLdsLimit = 160 * 1024;
+
+}  // namespace
+
+bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per_dir) {
+  if (p.B < 1 || p.B > kMaxNB || p.S < 1 || p.steps < 1) return false;
+  if (p.H > 8192) return false;
+  const int Gp = p.G - ((p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget) ? 1 : 0);
+  const int NB = next_pow2_nb(int(p.B));
+  const int maxw = 256 / p.D;  // one workgroup per compute unit
+  // about 64 R rows per workgroup (two per lane group); RNN_PERSISTENT_UNITS overrides for tuning
+  int U = std::max(1, 64 / Gp);
+  if (const char* env = std::getenv("RNN_PERSISTENT_UNITS")) U = std::max(1, std::atoi(env));
+  U = std::min(U, 64 / NB);
+  int wpd = int((p.H + U - 1) / U);
+  if (wpd > maxw) {
+    wpd = maxw;
+    U = int((p.H + wpd - 1) / wpd);
+    wpd = int((p.H + U - 1) / U);
+  }
+  if (U * NB > 64) return false;  // one gate thread per (unit, batch row), all in wave 0
+  if (lds_bytes(Gp * U, int(p.H), p.esize, NB) > kLdsLimit) return false;
+  *blocks = wpd * p.D;
+  *units = U;
+  *wg_per_dir = wpd;
+  return true;
+}
+
+template <typename T, int NB, bool DEF>
+static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStream_t s) {
+  auto kern = persistent_kernel<T, NB, DEF>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  PersArgs arg = pa;
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(blocks), dim3(kPThreads), args,
+                                    unsigned(lds), s);
+}
+
+hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const PersistentIO& io, hipStream_t s) {
+  PersArgs pa{};
+  pa.a = a;
+  pa.U = p.pers_units;
+  pa.WPD = p.pers_wg_per_dir;
+  const bool skip_f = p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget;
+  pa.Gp = p.G - (skip_f ? 1 : 0);
+  int gi = 0;
+  for (int g = 0; g < p.G; ++g) {
+    if (skip_f && g == 2) continue;
+    pa.gate_of[gi++] = g;
+  }
+  pa.NR = pa.Gp * pa.U;
+  pa.cand = (p.desc.cell == RNN_CELL_GRU && !p.desc.linear_before_reset) ? 2 : -1;
+  pa.layout = p.desc.layout;
+  pa.init_h = io.init_h;
+  pa.init_c = io.init_c;
+  pa.Y = io.Y;
+  pa.Y_h = io.Y_h;
+  pa.Y_c = io.Y_c;
+  pa.status = io.status;
+  const int NB = next_pow2_nb(a.B);
+  const size_t lds = lds_bytes(pa.NR, a.H, p.esize, NB);
+  const int blocks = p.pers_blocks;
+  const bool def = default_acts(p);
+#define RNN_PERS_CASE(T, NB)                                                      \
+  return def ? launch_nb<T, NB, true>(pa, blocks, lds, s) : launch_nb<T, NB, false>(pa, blocks, lds, s)
+  if (a.dtype == RNN_DTYPE_F32) {
+    switch (NB) {
+      case 1: RNN_PERS_CASE(float, 1);
+      case 2: RNN_PERS_CASE(float, 2);
+      case 4: RNN_PERS_CASE(float, 4);
+      default: RNN_PERS_CASE(float, 8);
+    }
+  }
+  switch (NB) {
+    case 1: RNN_PERS_CASE(half_t, 1);
+    case 2: RNN_PERS_CASE(half_t, 2);
+    case 4: RNN_PERS_CASE(half_t, 4);
+    default: RNN_PERS_CASE(half_t, 8);
+  }
+#undef RNN_PERS_CASE
+}
 
 }  // namespace rnnhip

@@ -7,7 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
-#include "../../include/rnn.h"
+#include "rnn.h"
 
 namespace rnnhip {
 
@@ -27,6 +27,7 @@ struct StateLayout {
   size_t rhbuf;    // f32 GRU r*h for the two-phase step: [D][B][H]
   size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
   size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
+  size_t status;   // int: persistent engine status (1: a wait hit its safety bound)
   size_t total;
 };
 
@@ -89,9 +90,21 @@ struct SetupArgs {
   int dtype;
   const void* init_h;  // or null
   const void* init_c;  // or null
-  float* slab;         // slot 0
-  float* cell_state;
-  unsigned long long* xch;   // or null (no persistent engine)
+  float* slab;         // slot 0, or null (persistent engine)
+  float* cell_state;   // or null (persistent engine)
+  unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
+  unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
+  int* status;               // persistent engine status word, or null
+};
+
+// What the persistent engine reads and writes besides StepArgs.
+struct PersistentIO {
+  const void* init_h;
+  const void* init_c;
+  void* Y;
+  void* Y_h;
+  void* Y_c;
+  int* status;
 };
 
 struct OutputArgs {
@@ -113,7 +126,7 @@ hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
 hipError_t launch_output(const OutputArgs& a, hipStream_t s);
 hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
-hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, hipStream_t s);
+hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const PersistentIO& io, hipStream_t s);
 bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per_dir);
 
 }  // namespace rnnhip

@@ -14,7 +14,12 @@ from tests.gpu_harness import gpu_layer, compare, oracle_rows, select_rows, note
 
 pytestmark = pytest.mark.gpu
 
-ENGINES = ["launch"]
+ENGINES = ["launch", "persistent"]
+
+
+def batch_for(engine, b_launch):
+    """The persistent engine takes batches up to 8; the per-step one any batch."""
+    return b_launch if engine == "launch" else min(b_launch, 7)
 
 
 def check(spec, inputs, engine="auto", offsets=None, twice=True, what=""):
@@ -66,14 +71,14 @@ for cell, direction, layout, dtype in itertools.product(("LSTM", "GRU", "RNN"),
 def test_matrix_options(cell, direction, layout, dtype, engine):
     lbrs = (0, 1) if cell == "GRU" else (0,)
     for lbr in lbrs:
-        spec = LayerSpec(cell, seq=9, batch=11, input=70, hidden=37, direction=direction, layout=layout,
+        spec = LayerSpec(cell, seq=9, batch=batch_for(engine, 11), input=70, hidden=37, direction=direction, layout=layout,
                          dtype=dtype, linear_before_reset=lbr, init_h=True, init_c=cell == "LSTM",
                          lens=True, peephole=cell == "LSTM", clip=2.5,
                          outputs=("Y", "Y_h", "Y_c"))
         inp = make_inputs(spec, 17, Dists(sequence_lens=("I", 0, 9), W=("U", -0.3, 0.3), R=("U", -0.3, 0.3)))
         check(spec, inp, engine=engine, what=f"{cell}/{direction}/L{layout}/{dtype}/lbr{lbr}")
     if cell == "LSTM":
-        spec = LayerSpec(cell, seq=6, batch=9, input=33, hidden=70, direction=direction, layout=layout,
+        spec = LayerSpec(cell, seq=6, batch=batch_for(engine, 9), input=33, hidden=70, direction=direction, layout=layout,
                          dtype=dtype, input_forget=1, peephole=True, bias=False, lens=False)
         check(spec, make_inputs(spec, 18), engine=engine, what=f"LSTM input_forget {direction} L{layout} {dtype}")
 
@@ -141,9 +146,9 @@ def test_lengths_edge_cases_and_max_length(engine):
 @pytest.mark.parametrize("engine", ENGINES)
 def test_batch_above_eight_and_hidden_not_dividing(engine):
     for cell, H in (("LSTM", 65), ("GRU", 127), ("RNN", 129)):
-        spec = LayerSpec(cell, seq=5, batch=19, input=31, hidden=H, direction="bidirectional", init_h=True,
-                         lens=True, linear_before_reset=0)
-        check(spec, make_inputs(spec, 21), engine=engine, what=f"B19 H{H} {cell}")
+        spec = LayerSpec(cell, seq=5, batch=19 if engine == "launch" else 8, input=31, hidden=H,
+                         direction="bidirectional", init_h=True, lens=True, linear_before_reset=0)
+        check(spec, make_inputs(spec, 21), engine=engine, what=f"B{spec.batch} H{H} {cell}")
 
 
 # ---------------------------------------------------------------------------
@@ -154,12 +159,28 @@ FULL = [("C1", {}), ("C2", {}), ("C3", {"linear_before_reset": 0}), ("C3", {"lin
 SAMPLE_ROWS = {"C4": [0, 9, 31, 63], "C5": [0, 255]}
 
 
-@pytest.mark.parametrize("name,over", FULL, ids=[f"{n}-{o}" for n, o in FULL])
+def test_engine_choice_and_plan():
+    import onnx_recurrent_layers_amd as rl
+    for name in ("C1", "C2", "C3"):
+        spec, _ = synth.config(name)
+        layer = rl.Layer(spec, engine="auto", device="cuda:0")
+        assert layer.plan.engine == rl.ENGINES["persistent"], name
+        assert layer.plan.step_launches == 1
+    for name in ("C4", "C5"):
+        spec, _ = synth.config(name)
+        layer = rl.Layer(spec, engine="auto", device="cuda:0")
+        assert layer.plan.engine == rl.ENGINES["launch"], name
+
+
+@pytest.mark.parametrize("name,over", FULL + [("C2", {"engine": "launch"}), ("C3", {"engine": "launch"})],
+                         ids=[f"{n}-{o}" for n, o in FULL + [("C2", {"engine": "launch"}), ("C3", {"engine": "launch"})]])
 def test_full_config(name, over):
+    over = dict(over)
+    engine = over.pop("engine", "auto")
     spec, inp = synth.config(name, **over)
-    note(f"case {name} {over} engine=auto")
-    got = gpu_layer(spec, inp, engine="auto")
-    again = gpu_layer(spec, inp, engine="auto")
+    note(f"case {name} {over} engine={engine}")
+    got = gpu_layer(spec, inp, engine=engine)
+    again = gpu_layer(spec, inp, engine=engine)
     for n in got:
         assert np.array_equal(got[n].view(np.uint8), again[n].view(np.uint8)), f"{name} {n}: runs differ"
     rows = SAMPLE_ROWS.get(name)
