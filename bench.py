@@ -59,6 +59,31 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+# Measured HBM traffic of the persistent step kernel on the default workload,
+# from two rocprofv3 counter runs (see the profile file); it is reported only
+# while the kernel sources still hash to what was profiled.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "persistent_step_bilstm_s80_b1_h256_f32.md")
+
+
+def profiled_traffic(path: str):
+    import hashlib
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    fields = dict(ln.split(": ", 1) for ln in text.splitlines()
+                  if ln.startswith(("traffic_bytes_per_launch", "kernel_sources_sha256_16", "kernel_sources")))
+    try:
+        h = hashlib.sha256()
+        for f in fields["kernel_sources"].split(", "):
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != fields["kernel_sources_sha256_16"].strip():
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def step_bytes(spec) -> int:
     """Algorithmic bytes of one recurrent step (both directions): R once, the
     step's slice of Xw, the previous h read and the new h written (plus the
@@ -81,6 +106,9 @@ def main() -> int:
     ap.add_argument("--engine", default="auto", choices=["auto", "launch", "persistent"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the layer, run a plain device copy of this many bytes (a known-size "
+                         "kernel against which the HBM byte counters of a profiler are scaled)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library runs a layer on a single MI355X "
@@ -92,6 +120,16 @@ def main() -> int:
     import torch
     import onnx_recurrent_layers_amd as rl
     from onnx_recurrent_layers_amd import synth
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return 0
 
     spec, inputs = synth.config(args.config)
     name = synth.CONFIGS[args.config]["name"]
@@ -160,7 +198,9 @@ def main() -> int:
         "stage_ms_median": {k: round(v, 5) for k, v in med.items()},
         "roofline": {
             "bound": "hbm", "kernel": "recurrent step", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+            "traffic": (profiled_traffic(TRAFFIC_PROFILE)
+                        if (args.config == "C2" and engine_name == "persistent") else None),
             "bytes_per_launch": int(bytes_per_launch), "launch_us": round(launch_ms * 1000.0, 3),
             "launches_per_layer": step_launches,
         },

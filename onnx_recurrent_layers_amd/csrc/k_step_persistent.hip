@@ -484,6 +484,26 @@ static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStrea
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
   PersArgs arg = pa;
+  // RNN_PLAIN_LAUNCH=1 launches the same kernel and grid without the
+  // cooperative API, after checking on the host that every workgroup fits on
+  // the chip at once.  It exists for profilers that fail on cooperative
+  // launches; the default is the cooperative launch, which guarantees that
+  // all workgroups are resident together.
+  static const bool plain = [] {
+    const char* e = std::getenv("RNN_PLAIN_LAUNCH");
+    return e && e[0] == '1';
+  }();
+  if (plain) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kPThreads,
+                                                           lds)) != hipSuccess)
+      return e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if (per_cu * cus < blocks) return hipErrorCooperativeLaunchTooLarge;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kPThreads), lds, s, arg);
+    return hipGetLastError();
+  }
   void* args[] = {&arg};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(blocks), dim3(kPThreads), args,
                                     unsigned(lds), s);
