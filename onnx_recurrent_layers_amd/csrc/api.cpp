@@ -393,8 +393,10 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
       if ((e = launch_step_persistent(a, p, io, s)) != hipSuccess)
         return fail(RNN_ERR_HIP, cell, "persistent step launch: %s", hipGetErrorString(e));
     } else {
+      // batches of 16 and more: the product of each step on the matrix cores
+      const bool mfma = mfma_step_supported(p);
       for (int step = 0; step < int(p.steps); ++step)
-        if ((e = launch_step_generic(a, step, s)) != hipSuccess)
+        if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
           return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));
     }
   }

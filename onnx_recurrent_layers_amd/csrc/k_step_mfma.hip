@@ -1,0 +1,338 @@
+// k_step_mfma.hip -- stage 3 of a layer ("Recurrent layers" page, "How a
+// layer runs", item 3) for larger batches: one launch per step (two for a GRU
+// with linear_before_reset = 0), each computing the recurrent product of the
+// step as a matrix product on the matrix cores and finishing the gate
+// arithmetic of cells.h in the epilogue.
+//
+// A workgroup owns a tile of BM batch rows x UJ hidden units of one direction
+// and all Gp gate blocks of those units, so the gate arithmetic needs no data
+// from other workgroups: the product tile is [BM] x [Gp*UJ] over K = H, with
+// A = h_prev rows (f32) and B = R rows (f32, or f16 widened exactly).
+// v_mfma_f32_16x16x4_f32 keeps exact f32 products with f32 accumulation;
+// the k order inside a workgroup is fixed (chunks of 64 in increasing order,
+// the instruction's own order within a chunk), so runs are bit-identical.
+// Operand chunks are staged through LDS, the next chunk is fetched into
+// registers while the current one feeds the matrix cores.
+#include "cells.h"
+
+namespace rnnhip {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMThreads = 256;
+constexpr int kBK = 64;          // k chunk
+constexpr int kLDA = kBK + 4;    // padded LDS row (floats)
+constexpr int kMaxNC = 128;      // gate rows per tile (Gp * UJ)
+constexpr int kSeg = 4;          // elements per load segment (16 bytes of f32 h; 8 bytes of f16 R, 16 of f32 R)
+
+struct MfmaStepArgs {
+  StepArgs a;
+  int UJ;           // units per tile (multiple of 16)
+  int Gp;           // gate blocks computed in this phase
+  int gate_of[4];   // gate block index of each computed block
+  int phase;        // GRU linear_before_reset = 0: 0 = z and r, 1 = candidate; else 0
+  int step;
+};
+
+// Four consecutive elements as f32 (vector load when aligned, else four loads).
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float* p) {
+  if constexpr (VEC) return *reinterpret_cast<const float4*>(p);
+  else return make_float4(p[0], p[1], p[2], p[3]);
+}
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const half_t* p) {
+  if constexpr (VEC) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 v = *reinterpret_cast<const h4*>(p);
+    return make_float4(float(v[0]), float(v[1]), float(v[2]), float(v[3]));
+  } else {
+    return make_float4(float(p[0]), float(p[1]), float(p[2]), float(p[3]));
+  }
+}
+
+template <typename T, int BM, bool VEC>
+__global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
+  const StepArgs& a = m.a;
+  const int H = a.H, B = a.B, G = a.G, S = a.S;
+  const int s = m.step;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = blockIdx.x * m.UJ;
+  const int b0 = blockIdx.y * BM;
+  const int d = blockIdx.z;
+  const int UJ = m.UJ, NC = m.Gp * UJ;
+
+  // rows of this tile that are still running at this step
+  __shared__ int len_s[BM];
+  __shared__ int any_s;
+  if (tid == 0) any_s = 0;
+  __syncthreads();
+  for (int r = tid; r < BM; r += kMThreads) {
+    const int b = b0 + r;
+    len_s[r] = b < B ? row_length(a.lens, b, S, a.steps) : 0;
+    if (s < len_s[r]) atomicOr(&any_s, 1);
+  }
+  __syncthreads();
+  if (!any_s) return;
+
+  __shared__ __attribute__((aligned(16))) float As[2][BM * kLDA];
+  __shared__ __attribute__((aligned(16))) float Bs[2][kMaxNC * kLDA];
+  __shared__ float rec[BM * (kMaxNC + 1)];
+
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * G * H * H;
+
+  // Staging: segment q of a chunk is row q / (kBK/kSeg), elements
+  // kSeg*(q % (kBK/kSeg)) .. +kSeg.  Each thread keeps the row pointers of its
+  // segments for the whole k loop.  Rows beyond the tile, ended batch rows
+  // and k beyond H read as zero (H is padded to the chunk by the valid mask).
+  constexpr int kSegRow = kBK / kSeg;
+  constexpr int kAPer = (BM * kSegRow + kMThreads - 1) / kMThreads;
+  constexpr int kBPer = (kMaxNC * kSegRow + kMThreads - 1) / kMThreads;
+  const float* aptr[kAPer];
+  const T* bptr[kBPer];
+  int aoff[kAPer], boff[kBPer];
+#pragma unroll
+  for (int i = 0; i < kAPer; ++i) {
+    const int q = tid + i * kMThreads;
+    const int r = q / kSegRow;
+    aoff[i] = (q % kSegRow) * kSeg;
+    const bool ok = q < BM * kSegRow && b0 + r < B && s < len_s[r];
+    aptr[i] = ok ? hsrc + int64_t(b0 + r) * H : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < kBPer; ++i) {
+    const int q = tid + i * kMThreads;
+    const int c = q / kSegRow;
+    boff[i] = (q % kSegRow) * kSeg;
+    bptr[i] = nullptr;
+    if (q < NC * kSegRow) {
+      const int gi = c / UJ, u = c - gi * UJ;
+      if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
+    }
+  }
+  float4 ra[kAPer], rb[kBPer];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int k = k0 + aoff[i];
+      ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (aptr[i]) {
+        if (k + kSeg <= H) ra[i] = load4<true>(aptr[i] + k);
+        else {
+          float t4[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int z = 0; z < kSeg && k + z < H; ++z) t4[z] = aptr[i][k + z];
+          ra[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int k = k0 + boff[i];
+      rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bptr[i]) {
+        if (k + kSeg <= H) rb[i] = load4<VEC>(bptr[i] + k);
+        else {
+          float t4[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int z = 0; z < kSeg && k + z < H; ++z) t4[z] = static_cast<float>(bptr[i][k + z]);
+          rb[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        }
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int q = tid + i * kMThreads;
+      if (q < BM * kSegRow) *reinterpret_cast<float4*>(&As[buf][(q / kSegRow) * kLDA + aoff[i]]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int q = tid + i * kMThreads;
+      if (q < NC * kSegRow) *reinterpret_cast<float4*>(&Bs[buf][(q / kSegRow) * kLDA + boff[i]]) = rb[i];
+    }
+  };
+
+  // 16x16 output blocks, dealt to the waves round-robin
+  const int nbm = BM / 16, nbn = NC / 16, nblk = nbm * nbn;
+  constexpr int kMaxBlk = (BM / 16) * (kMaxNC / 16) / 4 + 1;
+  f32x4 acc[kMaxBlk];
+#pragma unroll
+  for (int q = 0; q < kMaxBlk; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int nk = (H + kBK - 1) / kBK;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) fetch((kc + 1) * kBK);
+    const float* A = As[buf];
+    const float* Bm = Bs[buf];
+#pragma unroll
+    for (int q = 0; q < kMaxBlk; ++q) {
+      const int blk = wave + 4 * q;
+      if (blk >= nblk) break;
+      const int bi = blk / nbn, ci = blk - bi * nbn;
+      const float* arow = A + (bi * 16 + (lane & 15)) * kLDA + (lane >> 4);
+      const float* brow = Bm + (ci * 16 + (lane & 15)) * kLDA + (lane >> 4);
+#pragma unroll
+      for (int kk = 0; kk < kBK; kk += 4)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[kk], brow[kk], acc[q], 0, 0, 0);
+    }
+    if (kc + 1 < nk) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator layout of 16x16x4: element i of lane l is row 4*(l/16) + i, column l%16
+  constexpr int LDR = kMaxNC + 1;
+#pragma unroll
+  for (int q = 0; q < kMaxBlk; ++q) {
+    const int blk = wave + 4 * q;
+    if (blk >= nblk) break;
+    const int bi = blk / nbn, ci = blk - bi * nbn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc[q][i];
+  }
+  __syncthreads();
+
+  // gate arithmetic: one thread per (batch row, unit) of the tile
+  const int GH = G * H;
+  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
+  const Act* acts = a.act + d * a.slots;
+  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
+  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
+  for (int e = tid; e < BM * UJ; e += kMThreads) {
+    const int r = e / UJ, u = e - r * UJ;
+    const int b = b0 + r, j = j0 + u;
+    if (b >= B || j >= H) continue;
+    const int L = len_s[r];
+    if (s >= L) continue;
+    const int t = a.dir_reverse[d] ? (L - 1 - s) : s;
+    const float* xw = a.xw + ((int64_t(d) * S + t) * B + b) * GH;
+    const int64_t sidx = int64_t(b) * H + j;
+    const float* rrow = rec + r * LDR;
+    auto pre = [&](int gi, int g) {
+      const int n = g * H + j;
+      const float wb = bias ? ld(bias, n) : 0.f;
+      const float rbv = bias ? ld(bias, GH + n) : 0.f;
+      return pre_sum(xw[n], rrow[gi * UJ + u], wb, rbv);
+    };
+    if (a.cell == RNN_CELL_LSTM) {
+      float p4[4];
+      p4[0] = pre(0, 0);
+      p4[1] = pre(1, 1);
+      if (a.input_forget) {
+        p4[2] = 0.f;
+        p4[3] = pre(2, 3);
+      } else {
+        p4[2] = pre(2, 2);
+        p4[3] = pre(3, 3);
+      }
+      float peep[3];
+      const float* pp = nullptr;
+      if (a.P) {
+        const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
+        peep[0] = ld(P, j);
+        peep[1] = ld(P, H + j);
+        peep[2] = ld(P, 2 * H + j);
+        pp = peep;
+      }
+      float* cst = a.cell_state + dBH + sidx;
+      float h, c;
+      lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
+      *cst = c;
+      hnext[sidx] = h;
+    } else if (a.cell == RNN_CELL_GRU) {
+      if (a.lbr) {
+        // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+        const float z = gru_gate(pre(0, 0), a.clip, acts);
+        const float rg = gru_gate(pre(1, 1), a.clip, acts);
+        const int n = 2 * H + j;
+        const float wb = bias ? ld(bias, n) : 0.f;
+        const float rbv = bias ? ld(bias, GH + n) : 0.f;
+        const float ph = (xw[n] + rg * (rrow[2 * UJ + u] + rbv)) + wb;
+        hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+      } else if (m.phase == 0) {
+        const float z = gru_gate(pre(0, 0), a.clip, acts);
+        const float rg = gru_gate(pre(1, 1), a.clip, acts);
+        a.zbuf[dBH + sidx] = z;
+        a.rhbuf[dBH + sidx] = rg * hprev[sidx];
+      } else {
+        // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
+        const int n = 2 * H + j;
+        const float wb = bias ? ld(bias, n) : 0.f;
+        const float rbv = bias ? ld(bias, GH + n) : 0.f;
+        const float ph = pre_sum(xw[n], rrow[u], wb, rbv);
+        hnext[sidx] = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
+      }
+    } else {
+      hnext[sidx] = rnn_unit(pre(0, 0), a.clip, acts);
+    }
+  }
+}
+
+// Tile shape (BM batch rows, UJ units): the largest tile that still gives at
+// least 256 workgroups, so every compute unit has work.
+void mfma_tile(int B, int H, int D, int Gp, int* bm, int* uj) {
+  static const int cand[][2] = {{64, 64}, {64, 32}, {32, 32}, {32, 16}, {16, 16}};
+  for (const auto& c : cand) {
+    if (Gp * c[1] > kMaxNC) continue;
+    const long wgs = long((B + c[0] - 1) / c[0]) * ((H + c[1] - 1) / c[1]) * D;
+    *bm = c[0];
+    *uj = c[1];
+    if (wgs >= 256) return;
+  }
+}
+
+bool mfma_step_supported(const Problem& p) { return p.B >= 16; }
+
+template <typename T, int BM>
+static hipError_t launch_bm(const MfmaStepArgs& m, int H, int B, int D, hipStream_t s) {
+  const dim3 grid(unsigned((H + m.UJ - 1) / m.UJ), unsigned((B + BM - 1) / BM), unsigned(D));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  // vector loads of R need every row start aligned to a whole segment
+  const bool vec = (reinterpret_cast<uintptr_t>(m.a.R) % (kSeg * sizeof(T))) == 0 && H % kSeg == 0;
+  if (vec)
+    hipLaunchKernelGGL((step_mfma_kernel<T, BM, true>), grid, dim3(kMThreads), 0, s, m);
+  else
+    hipLaunchKernelGGL((step_mfma_kernel<T, BM, false>), grid, dim3(kMThreads), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s) {
+  const bool skip_f = a.cell == RNN_CELL_LSTM && a.input_forget;
+  const bool two_phase = a.cell == RNN_CELL_GRU && !a.lbr;
+  for (int ph = 0; ph < (two_phase ? 2 : 1); ++ph) {
+    MfmaStepArgs m{};
+    m.a = a;
+    m.step = step;
+    m.phase = ph;
+    int gi = 0;
+    for (int g = 0; g < a.G; ++g) {
+      if (skip_f && g == 2) continue;
+      if (two_phase && ph == 0 && g == 2) continue;
+      if (two_phase && ph == 1 && g != 2) continue;
+      m.gate_of[gi++] = g;
+    }
+    m.Gp = gi;
+    int bm = 16, uj = 16;
+    mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
+    m.UJ = uj;
+    hipError_t e;
+    if (a.dtype == RNN_DTYPE_F32) {
+      e = bm == 64 ? launch_bm<float, 64>(m, a.H, a.B, a.D, s)
+                   : bm == 32 ? launch_bm<float, 32>(m, a.H, a.B, a.D, s) : launch_bm<float, 16>(m, a.H, a.B, a.D, s);
+    } else {
+      e = bm == 64 ? launch_bm<half_t, 64>(m, a.H, a.B, a.D, s)
+                   : bm == 32 ? launch_bm<half_t, 32>(m, a.H, a.B, a.D, s) : launch_bm<half_t, 16>(m, a.H, a.B, a.D, s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rnnhip

@@ -126,6 +126,8 @@ hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
 hipError_t launch_output(const OutputArgs& a, hipStream_t s);
 hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
+hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);
+bool mfma_step_supported(const Problem& p);
 hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const PersistentIO& io, hipStream_t s);
 bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per_dir);
 

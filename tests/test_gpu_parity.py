@@ -83,6 +83,25 @@ def test_matrix_options(cell, direction, layout, dtype, engine):
         check(spec, make_inputs(spec, 18), engine=engine, what=f"LSTM input_forget {direction} L{layout} {dtype}")
 
 
+LARGE = [(c, d, dt) for c in ("LSTM", "GRU", "RNN") for d in ("forward", "bidirectional") for dt in ("f32", "f16")]
+
+
+@pytest.mark.parametrize("cell,direction,dtype", LARGE, ids=["-".join(m) for m in LARGE])
+def test_large_batch_matrix_engine(cell, direction, dtype):
+    """Batches of 16 and more take the matrix-core step kernel: ragged batch
+    and hidden sizes, every option, both GRU forms, both layouts."""
+    for lbr, layout, B, H in ((0, 0, 37, 50), (1, 1, 70, 33), (0, 1, 16, 130)):
+        if cell != "GRU" and lbr == 1:
+            lbr = 0
+        spec = LayerSpec(cell, seq=7, batch=B, input=29, hidden=H, direction=direction, layout=layout,
+                         dtype=dtype, linear_before_reset=lbr if cell == "GRU" else 0, init_h=True,
+                         init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM", clip=2.0,
+                         input_forget=1 if (cell == "LSTM" and B == 70) else 0,
+                         outputs=("Y", "Y_h", "Y_c"))
+        inp = make_inputs(spec, 23, Dists(sequence_lens=("I", 0, 7), W=("U", -0.3, 0.3), R=("U", -0.3, 0.3)))
+        check(spec, inp, engine="launch", what=f"large {cell}/{direction}/{dtype}/lbr{lbr}/L{layout}/B{B}/H{H}")
+
+
 ALL_ACTS = [("Relu", 0, 0), ("Tanh", 0, 0), ("Sigmoid", 0, 0), ("Affine", 0.7, -0.2), ("LeakyRelu", 0.03, 0),
             ("ThresholdedRelu", 0.2, 0), ("ScaledTanh", 1.5, 0.5), ("HardSigmoid", 0.2, 0.5), ("Elu", 0.8, 0),
             ("Softsign", 0, 0), ("Softplus", 0, 0)]
