@@ -149,14 +149,22 @@ def main() -> int:
         layer.encode(allt)
     torch.cuda.synchronize()
 
+    # timed region: exactly K layers through rnn_encode, nothing else on the stream
     K = args.steps
-    ev = HipEvents(5 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        layer.encode(allt, events=ev.ev[5 * i:5 * i + 5], stream=stream)
+        layer.encode(allt, stream=stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # a second pass with the library's stage-boundary events, for the per-stage
+    # breakdown and the step kernel's duration (each mark adds a small gap)
+    ev = HipEvents(5 * K)
+    torch.cuda.synchronize()
+    for i in range(K):
+        layer.encode(allt, events=ev.ev[5 * i:5 * i + 5], stream=stream)
+    torch.cuda.synchronize()
 
     lat = [ev.ms(5 * i, 5 * i + 4) for i in range(K)]
     stage = {k: [ev.ms(5 * i + a, 5 * i + b) for i in range(K)]
@@ -194,7 +202,7 @@ def main() -> int:
         "config": {"workload": name, "seq": spec.seq, "batch": spec.batch, "input": spec.input,
                    "hidden": spec.hidden, "directions": spec.num_directions, "engine": engine_name,
                    "timesteps_per_layer": n_steps},
-        "latency_ms_median_events": round(statistics.median(lat), 5),
+        "latency_ms_median_with_stage_events": round(statistics.median(lat), 5),
         "stage_ms_median": {k: round(v, 5) for k, v in med.items()},
         "roofline": {
             "bound": "hbm", "kernel": "recurrent step", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

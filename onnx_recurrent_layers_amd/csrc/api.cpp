@@ -221,8 +221,7 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
   info->step_blocks = p->engine == RNN_ENGINE_PERSISTENT ? p->pers_blocks : 0;
   int n = 0;
   if (p->B > 0) {
-    if (p->S > 0) n += 1;          // projection
-    n += 1;                        // state setup
+    n += 1;                        // projection with the state setup (or the setup alone when Seq = 0)
     if (p->S > 0) n += step_launch_count(*p);
     if (p->engine != RNN_ENGINE_PERSISTENT) n += 1;  // output pass (the persistent engine writes outputs itself)
   }
@@ -379,12 +378,14 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     pa.D = p.D;
     pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
     pa.H = p.H;
-    if ((e = launch_projection(pa, p.desc.dtype, s)) != hipSuccess)
+    // the state setup rides in the same launch (extra workgroups)
+    if ((e = launch_projection(pa, sa, p.desc.dtype, s)) != hipSuccess)
       return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));
   }
   if ((e = mark(1)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
-  // 2. state setup
-  if ((e = launch_setup(sa, s)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "setup launch: %s", hipGetErrorString(e));
+  // 2. state setup (its own launch only when there is no projection)
+  if (p.S == 0 && (e = launch_setup(sa, s)) != hipSuccess)
+    return fail(RNN_ERR_HIP, cell, "setup launch: %s", hipGetErrorString(e));
   if ((e = mark(2)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
   // 3. recurrent steps
   if (p.S > 0 && p.steps > 0) {

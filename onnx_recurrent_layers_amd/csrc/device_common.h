@@ -78,4 +78,35 @@ __device__ __forceinline__ int row_length(const int32_t* lens, int b, int S, int
   return L < steps ? L : steps;
 }
 
+// Stage 2 ("Recurrent layers" page, "How a layer runs", item 2): the first
+// hidden and cell state from initial_h / initial_c or zeros, for one share of
+// the (d, b, j) elements (`part` of `parts` workgroups): slot 0 of the
+// per-step state, the cell state, and for the persistent engine the tagged
+// exchange words of step 0 with the other slots marked empty.
+template <typename T>
+__device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int parts) {
+  const int64_t DBH = int64_t(a.D) * a.B * a.H;
+  for (int64_t i = part * int64_t(blockDim.x) + threadIdx.x; i < DBH; i += int64_t(parts) * blockDim.x) {
+    const int64_t j = i % a.H;
+    const int64_t b = (i / a.H) % a.B;
+    const int64_t d = i / (int64_t(a.H) * a.B);
+    // ONNX state layout: 0 -> [D,B,H]; 1 -> [B,D,H]
+    const int64_t src = a.layout == 0 ? i : (b * a.D + d) * a.H + j;
+    const float h0 = a.init_h ? ld(static_cast<const T*>(a.init_h), src) : 0.f;
+    const float c0 = a.init_c ? ld(static_cast<const T*>(a.init_c), src) : 0.f;
+    if (a.slab) a.slab[i] = h0;
+    if (a.cell_state) a.cell_state[i] = c0;
+    if (a.xch) {
+      // word = (tag << 32) | value bits; slot 0 carries step 0, slot 1 no step yet.
+      a.xch[i] = (0ull << 32) | __float_as_uint(h0);
+      a.xch[DBH + i] = 0xffffffffull << 32;
+    }
+    if (a.xch2) {
+      a.xch2[i] = 0xffffffffull << 32;
+      a.xch2[DBH + i] = 0xffffffffull << 32;
+    }
+  }
+  if (a.status && part == 0 && threadIdx.x == 0) *a.status = 0;
+}
+
 }  // namespace rnnhip

@@ -2,13 +2,19 @@
 // layer runs", item 1): the input projection of every step and direction as
 // one batched matrix product Xw[d] = X . W[d]^T (W read as stored, [G*H, I],
 // i.e. the transposed-B form), f32 accumulation.  No bias is added here: the
-// biases enter the gate sum in the page's fixed order.
+// biases enter the gate sum in the page's fixed order.  The same launch also
+// carries the state setup (stage 2) in a few extra workgroups.
 //
-// MI355X design: 128x128 output tiles per 256-thread workgroup (four wave64s,
-// 64x64 each as 2x2 blocks of 32x32 MFMA), operands staged through LDS.
-// f16 tensors use v_mfma_f32_32x32x16_f16 (f16 products are exact in f32, f32
-// accumulate); f32 tensors use v_mfma_f32_32x32x2_f32.  Rows of X are gathered
-// per layout so that Xw is written time-major ([D][S][B][G*H], row t*B+b).
+// MI355X design: BMxBN output tiles per 256-thread workgroup (four wave64s in
+// 2x2, each a grid of 32x32 MFMA blocks); k chunks (64 for f16, 32 for f32)
+// staged through double-buffered LDS, with the next chunk's 16-byte loads in
+// flight while the matrix cores work on the current one.  f16 tensors use
+// v_mfma_f32_32x32x16_f16 (f16 products are exact in f32, f32 accumulate);
+// f32 tensors use v_mfma_f32_32x32x2_f32.  Rows of X are gathered per layout
+// so that Xw is written time-major ([D][S][B][G*H], row t*B+b).  Tiles that
+// fall entirely in a gate block nobody reads (input_forget's f) are skipped.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace rnnhip {
@@ -16,11 +22,13 @@ namespace rnnhip {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 128, kBN = 128;
-
 template <typename T> struct ProjCfg;
-template <> struct ProjCfg<half_t> { static constexpr int BK = 32, PAD = 8; };
-template <> struct ProjCfg<float> { static constexpr int BK = 16, PAD = 4; };
+template <> struct ProjCfg<half_t> { static constexpr int BK = 64, SEG = 8; };   // 16-byte segments
+template <> struct ProjCfg<float> { static constexpr int BK = 32, SEG = 4; };
+
+template <typename T> struct Seg;
+template <> struct Seg<half_t> { typedef f16x8 type; };
+template <> struct Seg<float> { typedef float4 type; };
 
 // Row m of the product (m = t*B + b) -> row of X in its layout.
 __device__ __forceinline__ int64_t x_row(int64_t m, int64_t S, int64_t B, int layout) {
@@ -29,106 +37,182 @@ __device__ __forceinline__ int64_t x_row(int64_t m, int64_t S, int64_t B, int la
   return b * S + t;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void projection_kernel(ProjArgs a) {
-  constexpr int BK = ProjCfg<T>::BK, LD = BK + ProjCfg<T>::PAD;
-  __shared__ __attribute__((aligned(16))) T As[kBM * LD];
-  __shared__ __attribute__((aligned(16))) T Bs[kBN * LD];
+template <typename T, bool VEC>
+__device__ __forceinline__ typename Seg<T>::type load_seg(const T* p, int64_t k, int64_t K) {
+  typedef typename Seg<T>::type V;
+  constexpr int SEG = ProjCfg<T>::SEG;
+  if (VEC && k + SEG <= K) return *reinterpret_cast<const V*>(p + k);
+  V v;
+#pragma unroll
+  for (int z = 0; z < SEG; ++z) v[z] = (k + z < K) ? p[k + z] : T(0.f);
+  return v;
+}
 
-  const int d = blockIdx.z;
-  const int64_t m0 = int64_t(blockIdx.x) * kBM;
-  const int64_t n0 = int64_t(blockIdx.y) * kBN;
-  // a whole tile inside a gate block nobody reads (input_forget's f) is skipped
-  if (a.skip_block >= 0 && n0 >= a.skip_block * a.H && n0 + kBN <= (a.skip_block + 1) * a.H) return;
+template <typename T, int BM, int BN, bool VEC>
+__global__ __launch_bounds__(256) void projection_kernel(ProjArgs a, SetupArgs sa, int gemm_blocks) {
+  constexpr int BK = ProjCfg<T>::BK, SEG = ProjCfg<T>::SEG, LD = BK + SEG;  // padded LDS row
+  constexpr int SEGROW = BK / SEG;
+  constexpr int APER = BM * SEGROW / 256, BPER = BN * SEGROW / 256;
+  constexpr int WM = BM / 2, WN = BN / 2;             // per-wave tile
+  constexpr int IM = WM / 32, IN = WN / 32;           // 32x32 blocks per wave
+  typedef typename Seg<T>::type V;
+  __shared__ __attribute__((aligned(16))) T As[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) T Bs[2][BN * LD];
+
+  // extra workgroups: the state setup of stage 2
+  if (int(blockIdx.x) >= gemm_blocks) {
+    setup_state<T>(sa, int(blockIdx.x) - gemm_blocks, int(gridDim.x) - gemm_blocks);
+    return;
+  }
+  const int64_t mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+  const int64_t lin = blockIdx.x;
+  const int64_t mi = lin % mt, ni = (lin / mt) % nt;
+  const int d = int(lin / (mt * nt));
+  const int64_t m0 = mi * BM, n0 = ni * BN;
+  if (a.skip_block >= 0 && n0 >= a.skip_block * a.H && n0 + BN <= (a.skip_block + 1) * a.H) return;
 
   const T* X = static_cast<const T*>(a.X);
   const T* W = static_cast<const T*>(a.W) + int64_t(d) * a.N * a.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[2][2];
+  // row pointers of this thread's segments (null: outside the matrix)
+  const T* ap[APER];
+  const T* bp[BPER];
+  int ak[APER], bk[BPER];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < APER; ++i) {
+    const int q = tid + i * 256, r = q / SEGROW;
+    ak[i] = (q % SEGROW) * SEG;
+    ap[i] = (m0 + r < a.M) ? X + x_row(m0 + r, a.S, a.B, a.layout) * a.K : nullptr;
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < BPER; ++i) {
+    const int q = tid + i * 256, r = q / SEGROW;
+    bk[i] = (q % SEGROW) * SEG;
+    bp[i] = (n0 + r < a.N) ? W + (n0 + r) * a.K : nullptr;
+  }
+  V ra[APER], rb[BPER];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      V z{};
+      ra[i] = ap[i] ? load_seg<T, VEC>(ap[i], k0 + ak[i], a.K) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      V z{};
+      rb[i] = bp[i] ? load_seg<T, VEC>(bp[i], k0 + bk[i], a.K) : z;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < APER; ++i) {
+      const int q = tid + i * 256;
+      *reinterpret_cast<V*>(&As[buf][(q / SEGROW) * LD + ak[i]]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPER; ++i) {
+      const int q = tid + i * 256;
+      *reinterpret_cast<V*>(&Bs[buf][(q / SEGROW) * LD + bk[i]]) = rb[i];
+    }
+  };
+
+  f32x16 acc[IM][IN];
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < IN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int64_t k0 = 0; k0 < a.K; k0 += BK) {
-    // stage A (X rows) and B (W rows) tiles; zero outside the matrices
-    for (int e = tid; e < kBM * BK; e += 256) {
-      const int r = e / BK, k = e % BK;
-      const int64_t m = m0 + r, kk = k0 + k;
-      T v = T(0.f);
-      if (m < a.M && kk < a.K) v = X[x_row(m, a.S, a.B, a.layout) * a.K + kk];
-      As[r * LD + k] = v;
-    }
-    for (int e = tid; e < kBN * BK; e += 256) {
-      const int r = e / BK, k = e % BK;
-      const int64_t n = n0 + r, kk = k0 + k;
-      T v = T(0.f);
-      if (n < a.N && kk < a.K) v = W[n * a.K + kk];
-      Bs[r * LD + k] = v;
-    }
-    __syncthreads();
+  const int64_t nk = (a.K + BK - 1) / BK;
+  if (nk > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int64_t kc = 0; kc < nk; ++kc) {
+    const int buf = int(kc & 1);
+    if (kc + 1 < nk) fetch((kc + 1) * BK);
+    const T* A = As[buf];
+    const T* Bm = Bs[buf];
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int ks = 0; ks < BK; ks += 16) {
-        f16x8 av[2], bv[2];
+        f16x8 av[IM], bv[IN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          av[i] = *reinterpret_cast<const f16x8*>(&As[(wm * 64 + i * 32 + (lane & 31)) * LD + ks + 8 * (lane >> 5)]);
+        for (int i = 0; i < IM; ++i)
+          av[i] = *reinterpret_cast<const f16x8*>(&A[(wm * WM + i * 32 + (lane & 31)) * LD + ks + 8 * (lane >> 5)]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bv[j] = *reinterpret_cast<const f16x8*>(&Bs[(wn * 64 + j * 32 + (lane & 31)) * LD + ks + 8 * (lane >> 5)]);
+        for (int j = 0; j < IN; ++j)
+          bv[j] = *reinterpret_cast<const f16x8*>(&Bm[(wn * WN + j * 32 + (lane & 31)) * LD + ks + 8 * (lane >> 5)]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < IM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < IN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < BK; ks += 2) {
-        float av[2], bv[2];
+        float av[IM], bv[IN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) av[i] = As[(wm * 64 + i * 32 + (lane & 31)) * LD + ks + (lane >> 5)];
+        for (int i = 0; i < IM; ++i) av[i] = A[(wm * WM + i * 32 + (lane & 31)) * LD + ks + (lane >> 5)];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bv[j] = Bs[(wn * 64 + j * 32 + (lane & 31)) * LD + ks + (lane >> 5)];
+        for (int j = 0; j < IN; ++j) bv[j] = Bm[(wn * WN + j * 32 + (lane & 31)) * LD + ks + (lane >> 5)];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < IM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < IN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (kc + 1 < nk) stash(buf ^ 1);
     __syncthreads();
   }
 
   // 32x32 accumulator layout: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
   float* out = a.xw + int64_t(d) * a.M * a.N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < IN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int64_t m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = n0 + wn * WN + j * 32 + (lane & 31);
         if (m < a.M && n < a.N) out[m * a.N + n] = acc[i][j][r];
       }
 }
 
-hipError_t launch_projection(const ProjArgs& a, int dtype, hipStream_t s) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  const int64_t mt = (a.M + kBM - 1) / kBM, nt = (a.N + kBN - 1) / kBN;
-  if (mt > 0x7fffffff || nt > 65535) return hipErrorInvalidValue;
-  dim3 grid(unsigned(mt), unsigned(nt), unsigned(a.D));
-  if (dtype == RNN_DTYPE_F32)
-    hipLaunchKernelGGL(projection_kernel<float>, grid, dim3(256), 0, s, a);
+template <typename T, int BM, int BN>
+static hipError_t launch_tile(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s) {
+  const int64_t mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+  const int64_t gemm = (a.M > 0 && a.N > 0) ? mt * nt * a.D : 0;
+  if (gemm + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int seg = ProjCfg<T>::SEG;
+  const bool vec = a.K % seg == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+  const dim3 grid(unsigned(gemm + setup_blocks));
+  if (vec)
+    hipLaunchKernelGGL((projection_kernel<T, BM, BN, true>), grid, dim3(256), 0, s, a, sa, int(gemm));
   else
-    hipLaunchKernelGGL(projection_kernel<half_t>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((projection_kernel<T, BM, BN, false>), grid, dim3(256), 0, s, a, sa, int(gemm));
   return hipGetLastError();
+}
+
+hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s) {
+  const int64_t n_state = int64_t(sa.D) * sa.B * sa.H;
+  const int setup_blocks = n_state > 0 ? int(std::min<int64_t>((n_state + 255) / 256, 1024)) : 0;
+  // 128x128 tiles when they still give every compute unit a workgroup, else 64x64
+  const int64_t big = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.D;
+  const bool use_big = big >= 256;
+  if (dtype == RNN_DTYPE_F32)
+    return use_big ? launch_tile<float, 128, 128>(a, sa, setup_blocks, s)
+                   : launch_tile<float, 64, 64>(a, sa, setup_blocks, s);
+  return use_big ? launch_tile<half_t, 128, 128>(a, sa, setup_blocks, s)
+                 : launch_tile<half_t, 64, 64>(a, sa, setup_blocks, s);
 }
 
 }  // namespace rnnhip

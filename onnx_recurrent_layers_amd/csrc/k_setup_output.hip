@@ -7,32 +7,9 @@
 
 namespace rnnhip {
 
-// One thread per (d, b, j): slot 0 of the per-step state, the cell state, and
-// (persistent engine) the tagged exchange words of step 0.
 template <typename T>
 __global__ void setup_kernel(SetupArgs a) {
-  const int64_t DBH = int64_t(a.D) * a.B * a.H;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < DBH; i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t j = i % a.H;
-    const int64_t b = (i / a.H) % a.B;
-    const int64_t d = i / (int64_t(a.H) * a.B);
-    // ONNX state layout: 0 -> [D,B,H]; 1 -> [B,D,H]
-    const int64_t src = a.layout == 0 ? i : (b * a.D + d) * a.H + j;
-    const float h0 = a.init_h ? ld(static_cast<const T*>(a.init_h), src) : 0.f;
-    const float c0 = a.init_c ? ld(static_cast<const T*>(a.init_c), src) : 0.f;
-    if (a.slab) a.slab[i] = h0;
-    if (a.cell_state) a.cell_state[i] = c0;
-    if (a.xch) {
-      // word = (tag << 32) | value bits; slot 0 carries step 0, slot 1 no step yet.
-      a.xch[i] = (0ull << 32) | __float_as_uint(h0);
-      a.xch[DBH + i] = 0xffffffffull << 32;
-    }
-    if (a.xch2) {
-      a.xch2[i] = 0xffffffffull << 32;
-      a.xch2[DBH + i] = 0xffffffffull << 32;
-    }
-  }
-  if (a.status && blockIdx.x == 0 && threadIdx.x == 0) *a.status = 0;
+  setup_state<T>(a, int(blockIdx.x), int(gridDim.x));
 }
 
 template <typename T>

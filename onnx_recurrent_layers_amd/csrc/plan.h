@@ -121,7 +121,7 @@ struct OutputArgs {
   void* Y_c;   // or null
 };
 
-hipError_t launch_projection(const ProjArgs& a, int dtype, hipStream_t s);
+hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s);  // also runs the state setup
 hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
 hipError_t launch_output(const OutputArgs& a, hipStream_t s);
 hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
