@@ -120,6 +120,13 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   if (desc->max_length < 0 || desc->max_length > desc->seq)
     return bad(RNN_ERR_SHAPE, "max_length: must be in [0, seq], got %lld", (long long)desc->max_length);
   p->steps = desc->max_length > 0 ? desc->max_length : desc->seq;
+  p->def_acts = true;
+  for (int d = 0; d < p->D; ++d)
+    for (int k = 0; k < p->slots; ++k) {
+      const int kind = desc->activations[d * p->slots + k].kind;
+      const int want = cell == RNN_CELL_RNN ? RNN_ACT_TANH : (k == 0 ? RNN_ACT_SIGMOID : RNN_ACT_TANH);
+      if (kind != want) p->def_acts = false;
+    }
   if (p->H > (int64_t(1) << 24)) return bad(RNN_ERR_UNSUPPORTED, "hidden: above 16777216");
   if (p->B > (int64_t(1) << 30)) return bad(RNN_ERR_UNSUPPORTED, "batch: above 2^30");
   if (p->S > (int64_t(1) << 30)) return bad(RNN_ERR_UNSUPPORTED, "seq: above 2^30");

@@ -51,6 +51,94 @@ __device__ __forceinline__ float4 load4(const half_t* p) {
   }
 }
 
+// Gate arithmetic of a finished product tile rec[BM][Gp*UJ] (row stride
+// kMaxNC + 1): one thread per (batch row, unit), in the order of cells.h.
+template <typename T, int BM>
+__device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float* rec, const int* len_s, int b0,
+                                              int j0, int d) {
+  const StepArgs& a = m.a;
+  const int H = a.H, B = a.B, G = a.G, S = a.S;
+  const int s = m.step;
+  const int tid = threadIdx.x;
+  const int UJ = m.UJ;
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  constexpr int LDR = kMaxNC + 1;
+  const int GH = G * H;
+  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
+  const Act* acts = a.act + d * a.slots;
+  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
+  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
+  for (int e = tid; e < BM * UJ; e += kMThreads) {
+    const int r = e / UJ, u = e - r * UJ;
+    const int b = b0 + r, j = j0 + u;
+    if (b >= B || j >= H) continue;
+    const int L = len_s[r];
+    if (s >= L) continue;
+    const int t = a.dir_reverse[d] ? (L - 1 - s) : s;
+    const float* xw = a.xw + ((int64_t(d) * S + t) * B + b) * GH;
+    const int64_t sidx = int64_t(b) * H + j;
+    const float* rrow = rec + r * LDR;
+    auto pre = [&](int gi, int g) {
+      const int n = g * H + j;
+      const float wb = bias ? ld(bias, n) : 0.f;
+      const float rbv = bias ? ld(bias, GH + n) : 0.f;
+      return pre_sum(xw[n], rrow[gi * UJ + u], wb, rbv);
+    };
+    if (a.cell == RNN_CELL_LSTM) {
+      float p4[4];
+      p4[0] = pre(0, 0);
+      p4[1] = pre(1, 1);
+      if (a.input_forget) {
+        p4[2] = 0.f;
+        p4[3] = pre(2, 3);
+      } else {
+        p4[2] = pre(2, 2);
+        p4[3] = pre(3, 3);
+      }
+      float peep[3];
+      const float* pp = nullptr;
+      if (a.P) {
+        const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
+        peep[0] = ld(P, j);
+        peep[1] = ld(P, H + j);
+        peep[2] = ld(P, 2 * H + j);
+        pp = peep;
+      }
+      float* cst = a.cell_state + dBH + sidx;
+      float h, c;
+      lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
+      *cst = c;
+      hnext[sidx] = h;
+    } else if (a.cell == RNN_CELL_GRU) {
+      if (a.lbr) {
+        // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+        const float z = gru_gate(pre(0, 0), a.clip, acts);
+        const float rg = gru_gate(pre(1, 1), a.clip, acts);
+        const int n = 2 * H + j;
+        const float wb = bias ? ld(bias, n) : 0.f;
+        const float rbv = bias ? ld(bias, GH + n) : 0.f;
+        const float ph = (xw[n] + rg * (rrow[2 * UJ + u] + rbv)) + wb;
+        hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+      } else if (m.phase == 0) {
+        const float z = gru_gate(pre(0, 0), a.clip, acts);
+        const float rg = gru_gate(pre(1, 1), a.clip, acts);
+        a.zbuf[dBH + sidx] = z;
+        a.rhbuf[dBH + sidx] = rg * hprev[sidx];
+      } else {
+        // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
+        const int n = 2 * H + j;
+        const float wb = bias ? ld(bias, n) : 0.f;
+        const float rbv = bias ? ld(bias, GH + n) : 0.f;
+        const float ph = pre_sum(xw[n], rrow[u], wb, rbv);
+        hnext[sidx] = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
+      }
+    } else {
+      hnext[sidx] = rnn_unit(pre(0, 0), a.clip, acts);
+    }
+  }
+}
+
 template <typename T, int BM, bool VEC>
 __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
   const StepArgs& a = m.a;
@@ -199,80 +287,185 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
   }
   __syncthreads();
 
-  // gate arithmetic: one thread per (batch row, unit) of the tile
-  const int GH = G * H;
-  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
-  const Act* acts = a.act + d * a.slots;
-  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
-  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
-  for (int e = tid; e < BM * UJ; e += kMThreads) {
-    const int r = e / UJ, u = e - r * UJ;
-    const int b = b0 + r, j = j0 + u;
-    if (b >= B || j >= H) continue;
-    const int L = len_s[r];
-    if (s >= L) continue;
-    const int t = a.dir_reverse[d] ? (L - 1 - s) : s;
-    const float* xw = a.xw + ((int64_t(d) * S + t) * B + b) * GH;
-    const int64_t sidx = int64_t(b) * H + j;
-    const float* rrow = rec + r * LDR;
-    auto pre = [&](int gi, int g) {
-      const int n = g * H + j;
-      const float wb = bias ? ld(bias, n) : 0.f;
-      const float rbv = bias ? ld(bias, GH + n) : 0.f;
-      return pre_sum(xw[n], rrow[gi * UJ + u], wb, rbv);
-    };
-    if (a.cell == RNN_CELL_LSTM) {
-      float p4[4];
-      p4[0] = pre(0, 0);
-      p4[1] = pre(1, 1);
-      if (a.input_forget) {
-        p4[2] = 0.f;
-        p4[3] = pre(2, 3);
-      } else {
-        p4[2] = pre(2, 2);
-        p4[3] = pre(3, 3);
-      }
-      float peep[3];
-      const float* pp = nullptr;
-      if (a.P) {
-        const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
-        peep[0] = ld(P, j);
-        peep[1] = ld(P, H + j);
-        peep[2] = ld(P, 2 * H + j);
-        pp = peep;
-      }
-      float* cst = a.cell_state + dBH + sidx;
-      float h, c;
-      lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
-      *cst = c;
-      hnext[sidx] = h;
-    } else if (a.cell == RNN_CELL_GRU) {
-      if (a.lbr) {
-        // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
-        const float z = gru_gate(pre(0, 0), a.clip, acts);
-        const float rg = gru_gate(pre(1, 1), a.clip, acts);
-        const int n = 2 * H + j;
-        const float wb = bias ? ld(bias, n) : 0.f;
-        const float rbv = bias ? ld(bias, GH + n) : 0.f;
-        const float ph = (xw[n] + rg * (rrow[2 * UJ + u] + rbv)) + wb;
-        hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
-      } else if (m.phase == 0) {
-        const float z = gru_gate(pre(0, 0), a.clip, acts);
-        const float rg = gru_gate(pre(1, 1), a.clip, acts);
-        a.zbuf[dBH + sidx] = z;
-        a.rhbuf[dBH + sidx] = rg * hprev[sidx];
-      } else {
-        // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
-        const int n = 2 * H + j;
-        const float wb = bias ? ld(bias, n) : 0.f;
-        const float rbv = bias ? ld(bias, GH + n) : 0.f;
-        const float ph = pre_sum(xw[n], rrow[u], wb, rbv);
-        hnext[sidx] = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
-      }
-    } else {
-      hnext[sidx] = rnn_unit(pre(0, 0), a.clip, acts);
+  mfma_epilogue<T, BM>(m, rec, len_s, b0, j0, d);
+}
+
+// f16 R on the f16 matrix cores.  R is exact in f16; each f32 value of h is
+// split into hi = f16(h) and lo = f16(h - hi), and the product is taken as
+// R.hi + R.lo with v_mfma_f32_16x16x32_f16 (f16 products are exact in f32,
+// f32 accumulation), so the only loss is lo's own rounding, about 2^-22 of |h|.
+// Used when every activation is the ONNX default, which keeps |h| within the
+// f16 range (|h| <= max(1, |initial h|)).
+constexpr int kBK16 = 128;           // k chunk (f16 path)
+constexpr int kLDH = kBK16 + 8;      // padded LDS row (halves)
+
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+
+template <int BM, bool VEC>
+__global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m) {
+  const StepArgs& a = m.a;
+  const int H = a.H, B = a.B, G = a.G, S = a.S;
+  const int s = m.step;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = blockIdx.x * m.UJ;
+  const int b0 = blockIdx.y * BM;
+  const int d = blockIdx.z;
+  const int UJ = m.UJ, NC = m.Gp * UJ;
+
+  __shared__ int len_s[BM];
+  __shared__ int any_s;
+  if (tid == 0) any_s = 0;
+  __syncthreads();
+  for (int r = tid; r < BM; r += kMThreads) {
+    const int b = b0 + r;
+    len_s[r] = b < B ? row_length(a.lens, b, S, a.steps) : 0;
+    if (s < len_s[r]) atomicOr(&any_s, 1);
+  }
+  __syncthreads();
+  if (!any_s) return;
+
+  // staging buffers; the product tile rec reuses their space after the k loop
+  constexpr int kAHalves = BM * kLDH, kBHalves = kMaxNC * kLDH;
+  constexpr int kPool = (4 * kAHalves + 2 * kBHalves) * 2;
+  static_assert(BM * (kMaxNC + 1) * 4 <= kPool, "product tile must fit in the staging space");
+  __shared__ __attribute__((aligned(16))) unsigned char pool[kPool];
+  half_t (*Ahi)[kAHalves] = reinterpret_cast<half_t (*)[kAHalves]>(pool);
+  half_t (*Alo)[kAHalves] = reinterpret_cast<half_t (*)[kAHalves]>(pool + 2 * kAHalves * 2);
+  half_t (*Bh)[kBHalves] = reinterpret_cast<half_t (*)[kBHalves]>(pool + 4 * kAHalves * 2);
+  float* rec = reinterpret_cast<float*>(pool);
+
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const half_t* Rd = static_cast<const half_t*>(a.R) + int64_t(d) * G * H * H;
+
+  // A: segments of 4 f32 (16 bytes); B: segments of 8 halves (16 bytes)
+  constexpr int kASegRow = kBK16 / 4, kBSegRow = kBK16 / 8;
+  constexpr int kAPer = (BM * kASegRow + kMThreads - 1) / kMThreads;
+  constexpr int kBPer = (kMaxNC * kBSegRow + kMThreads - 1) / kMThreads;
+  const float* aptr[kAPer];
+  const half_t* bptr[kBPer];
+  int aoff[kAPer], boff[kBPer];
+#pragma unroll
+  for (int i = 0; i < kAPer; ++i) {
+    const int q = tid + i * kMThreads;
+    const int r = q / kASegRow;
+    aoff[i] = (q % kASegRow) * 4;
+    const bool ok = q < BM * kASegRow && b0 + r < B && s < len_s[r];
+    aptr[i] = ok ? hsrc + int64_t(b0 + r) * H : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < kBPer; ++i) {
+    const int q = tid + i * kMThreads;
+    const int c = q / kBSegRow;
+    boff[i] = (q % kBSegRow) * 8;
+    bptr[i] = nullptr;
+    if (q < NC * kBSegRow) {
+      const int gi = c / UJ, u = c - gi * UJ;
+      if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
     }
   }
+  float4 ra[kAPer];
+  h16x8 rb[kBPer];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int k = k0 + aoff[i];
+      ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (aptr[i]) {
+        if (k + 4 <= H) ra[i] = *reinterpret_cast<const float4*>(aptr[i] + k);
+        else {
+          float t4[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int z = 0; z < 4 && k + z < H; ++z) t4[z] = aptr[i][k + z];
+          ra[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int k = k0 + boff[i];
+      h16x8 v;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) v[z] = half_t(0.f);
+      if (bptr[i]) {
+        if (VEC && k + 8 <= H) v = *reinterpret_cast<const h16x8*>(bptr[i] + k);
+        else
+          for (int z = 0; z < 8 && k + z < H; ++z) v[z] = bptr[i][k + z];
+      }
+      rb[i] = v;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int q = tid + i * kMThreads;
+      if (q < BM * kASegRow) {
+        const float x[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+        h16x4 hi, lo;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          hi[z] = half_t(x[z]);
+          lo[z] = half_t(x[z] - float(hi[z]));
+        }
+        const int off = (q / kASegRow) * kLDH + aoff[i];
+        *reinterpret_cast<h16x4*>(&Ahi[buf][off]) = hi;
+        *reinterpret_cast<h16x4*>(&Alo[buf][off]) = lo;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int q = tid + i * kMThreads;
+      if (q < NC * kBSegRow) *reinterpret_cast<h16x8*>(&Bh[buf][(q / kBSegRow) * kLDH + boff[i]]) = rb[i];
+    }
+  };
+
+  const int nbm = BM / 16, nbn = NC / 16, nblk = nbm * nbn;
+  constexpr int kMaxBlk = (BM / 16) * (kMaxNC / 16) / 4 + 1;
+  f32x4 acc[kMaxBlk];
+#pragma unroll
+  for (int q = 0; q < kMaxBlk; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int nk = (H + kBK16 - 1) / kBK16;
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) fetch((kc + 1) * kBK16);
+#pragma unroll
+    for (int q = 0; q < kMaxBlk; ++q) {
+      const int blk = wave + 4 * q;
+      if (blk >= nblk) break;
+      const int bi = blk / nbn, ci = blk - bi * nbn;
+      const int ao = (bi * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4);
+      const int bo = (ci * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4);
+#pragma unroll
+      for (int kk = 0; kk < kBK16; kk += 32) {
+        const h16x8 ah = *reinterpret_cast<const h16x8*>(&Ahi[buf][ao + kk]);
+        const h16x8 al = *reinterpret_cast<const h16x8*>(&Alo[buf][ao + kk]);
+        const h16x8 bv = *reinterpret_cast<const h16x8*>(&Bh[buf][bo + kk]);
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, acc[q], 0, 0, 0);
+      }
+    }
+    if (kc + 1 < nk) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator layout of the 16x16 MFMA: element i of lane l is row 4*(l/16) + i, column l%16
+  constexpr int LDR = kMaxNC + 1;
+#pragma unroll
+  for (int q = 0; q < kMaxBlk; ++q) {
+    const int blk = wave + 4 * q;
+    if (blk >= nblk) break;
+    const int bi = blk / nbn, ci = blk - bi * nbn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc[q][i];
+  }
+  __syncthreads();
+  mfma_epilogue<half_t, BM>(m, rec, len_s, b0, j0, d);
 }
 
 // Tile shape (BM batch rows, UJ units): the largest tile that still gives at
@@ -303,6 +496,18 @@ static hipError_t launch_bm(const MfmaStepArgs& m, int H, int B, int D, hipStrea
   return hipGetLastError();
 }
 
+template <int BM>
+static hipError_t launch_h16(const MfmaStepArgs& m, int H, int B, int D, hipStream_t s) {
+  const dim3 grid(unsigned((H + m.UJ - 1) / m.UJ), unsigned((B + BM - 1) / BM), unsigned(D));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  const bool vec = (reinterpret_cast<uintptr_t>(m.a.R) % 16) == 0 && H % 8 == 0;
+  if (vec)
+    hipLaunchKernelGGL((step_mfma_h16_kernel<BM, true>), grid, dim3(kMThreads), 0, s, m);
+  else
+    hipLaunchKernelGGL((step_mfma_h16_kernel<BM, false>), grid, dim3(kMThreads), 0, s, m);
+  return hipGetLastError();
+}
+
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s) {
   const bool skip_f = a.cell == RNN_CELL_LSTM && a.input_forget;
   const bool two_phase = a.cell == RNN_CELL_GRU && !a.lbr;
@@ -323,7 +528,10 @@ hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipSt
     mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
     m.UJ = uj;
     hipError_t e;
-    if (a.dtype == RNN_DTYPE_F32) {
+    if (a.dtype == RNN_DTYPE_F16 && p.def_acts) {
+      e = bm == 64 ? launch_h16<64>(m, a.H, a.B, a.D, s)
+                   : bm == 32 ? launch_h16<32>(m, a.H, a.B, a.D, s) : launch_h16<16>(m, a.H, a.B, a.D, s);
+    } else if (a.dtype == RNN_DTYPE_F32) {
       e = bm == 64 ? launch_bm<float, 64>(m, a.H, a.B, a.D, s)
                    : bm == 32 ? launch_bm<float, 32>(m, a.H, a.B, a.D, s) : launch_bm<float, 16>(m, a.H, a.B, a.D, s);
     } else {

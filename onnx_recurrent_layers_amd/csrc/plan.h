@@ -42,6 +42,7 @@ struct Problem {
   size_t xw_bytes = 0;
   StateLayout st{};
   int engine = RNN_ENGINE_LAUNCH;
+  bool def_acts = false;  // every activation slot holds the cell's ONNX default
   // persistent engine geometry
   int pers_blocks = 0;       // workgroups of the cooperative launch
   int pers_units = 0;        // units per workgroup

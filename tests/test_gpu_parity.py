@@ -102,6 +102,19 @@ def test_large_batch_matrix_engine(cell, direction, dtype):
         check(spec, inp, engine="launch", what=f"large {cell}/{direction}/{dtype}/lbr{lbr}/L{layout}/B{B}/H{H}")
 
 
+def test_large_batch_general_activations():
+    """The matrix-core step kernel with non-default activations (f16 tensors
+    then take the f32 path, f32 tensors always do)."""
+    for cell, acts in (("LSTM", (("HardSigmoid", 0.2, 0.5), ("Softsign", 0, 0), ("Elu", 0.9, 0))),
+                       ("GRU", (("Sigmoid", 0, 0), ("LeakyRelu", 0.05, 0))),
+                       ("RNN", (("Relu", 0, 0),))):
+        for dtype in ("f16", "f32"):
+            spec = LayerSpec(cell, seq=6, batch=33, input=20, hidden=48, direction="bidirectional", dtype=dtype,
+                             acts=acts, init_h=True, lens=True, linear_before_reset=1 if cell == "GRU" else 0)
+            check(spec, make_inputs(spec, 29, Dists(sequence_lens=("I", 0, 6))), engine="launch",
+                  what=f"large general acts {cell} {dtype}")
+
+
 ALL_ACTS = [("Relu", 0, 0), ("Tanh", 0, 0), ("Sigmoid", 0, 0), ("Affine", 0.7, -0.2), ("LeakyRelu", 0.03, 0),
             ("ThresholdedRelu", 0.2, 0), ("ScaledTanh", 1.5, 0.5), ("HardSigmoid", 0.2, 0.5), ("Elu", 0.8, 0),
             ("Softsign", 0, 0), ("Softplus", 0, 0)]
