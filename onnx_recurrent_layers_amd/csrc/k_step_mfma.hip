@@ -23,6 +23,7 @@ constexpr int kMThreads = 256;
 constexpr int kBK = 64;          // k chunk
 constexpr int kLDA = kBK + 4;    // padded LDS row (floats)
 constexpr int kMaxNC = 128;      // gate rows per tile (Gp * UJ)
+constexpr int kPF = 3;           // k chunks in flight
 constexpr int kSeg = 4;          // elements per load segment (16 bytes of f32 h; 8 bytes of f16 R, 16 of f32 R)
 
 struct MfmaStepArgs {
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
       if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
     }
   }
-  float4 ra[kAPer], rb[kBPer];
-  auto fetch = [&](int k0) {
+  float4 ring_a[kPF][kAPer], ring_b[kPF][kBPer];
+  auto fetch = [&](int k0, float4* ra, float4* rb) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int k = k0 + aoff[i];
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const float4* ra, const float4* rb) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int q = tid + i * kMThreads;
@@ -244,46 +245,71 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
     }
   };
 
-  // 16x16 output blocks, dealt to the waves round-robin
-  const int nbm = BM / 16, nbn = NC / 16, nblk = nbm * nbn;
-  constexpr int kMaxBlk = (BM / 16) * (kMaxNC / 16) / 4 + 1;
-  f32x4 acc[kMaxBlk];
+  // 16x16 output blocks: wave w owns column blocks w, w+4 (all row blocks of
+  // the tile), so its matrix-core instructions alternate between independent
+  // accumulators and share each loaded B operand across the row blocks
+  constexpr int NBI = BM / 16;
+  constexpr int CB = kMaxNC / 16 / 4;
+  const int ncb = NC / 16;
+  f32x4 acc[CB][NBI];
 #pragma unroll
-  for (int q = 0; q < kMaxBlk; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi) acc[cb][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  // k loop with kPF chunks in flight: chunk c lives in ring slot c % kPF from
+  // its fetch (iteration c - kPF) until it is staged in LDS (iteration c - 1)
   const int nk = (H + kBK - 1) / kBK;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) fetch((kc + 1) * kBK);
-    const float* A = As[buf];
-    const float* Bm = Bs[buf];
 #pragma unroll
-    for (int q = 0; q < kMaxBlk; ++q) {
-      const int blk = wave + 4 * q;
-      if (blk >= nblk) break;
-      const int bi = blk / nbn, ci = blk - bi * nbn;
-      const float* arow = A + (bi * 16 + (lane & 15)) * kLDA + (lane >> 4);
-      const float* brow = Bm + (ci * 16 + (lane & 15)) * kLDA + (lane >> 4);
+  for (int u = 0; u < kPF; ++u)
+    if (u < nk) fetch(u * kBK, ring_a[u], ring_b[u]);
+  stash(0, ring_a[0], ring_b[0]);
+  __syncthreads();
+  for (int kc0 = 0; kc0 < nk; kc0 += kPF) {
 #pragma unroll
-      for (int kk = 0; kk < kBK; kk += 4)
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[kk], brow[kk], acc[q], 0, 0, 0);
+    for (int u = 0; u < kPF; ++u) {
+      const int kc = kc0 + u;
+      if (kc >= nk) break;
+      const int buf = kc & 1;
+      const float* A = As[buf];
+      const float* Bm = Bs[buf];
+      float av[NBI][kBK / 4];
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int kk = 0; kk < kBK / 4; ++kk) av[bi][kk] = A[(bi * 16 + (lane & 15)) * kLDA + 4 * kk + (lane >> 4)];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int ci = wave + 4 * cb;
+        if (ci >= ncb) break;
+        float bv[kBK / 4];
+#pragma unroll
+        for (int kk = 0; kk < kBK / 4; ++kk) bv[kk] = Bm[(ci * 16 + (lane & 15)) * kLDA + 4 * kk + (lane >> 4)];
+#pragma unroll
+        for (int kk = 0; kk < kBK / 4; ++kk)
+#pragma unroll
+          for (int bi = 0; bi < NBI; ++bi)
+            acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[bi][kk], bv[kk], acc[cb][bi], 0, 0, 0);
+      }
+      const int nx = (u + 1) % kPF;
+      if (kc + 1 < nk) stash(buf ^ 1, ring_a[nx], ring_b[nx]);
+      // slot u held chunk kc, staged an iteration ago: it receives chunk kc + kPF
+      if (kc + kPF < nk) fetch((kc + kPF) * kBK, ring_a[u], ring_b[u]);
+      __syncthreads();
     }
-    if (kc + 1 < nk) stash(buf ^ 1);
-    __syncthreads();
   }
 
   // accumulator layout of 16x16x4: element i of lane l is row 4*(l/16) + i, column l%16
   constexpr int LDR = kMaxNC + 1;
 #pragma unroll
-  for (int q = 0; q < kMaxBlk; ++q) {
-    const int blk = wave + 4 * q;
-    if (blk >= nblk) break;
-    const int bi = blk / nbn, ci = blk - bi * nbn;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int ci = wave + 4 * cb;
+    if (ci >= ncb) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc[q][i];
+    for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc[cb][bi][i];
   }
   __syncthreads();
 
@@ -293,7 +319,8 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
 // f16 R on the f16 matrix cores.  R is exact in f16; each f32 value of h is
 // split into hi = f16(h) and lo = f16(h - hi), and the product is taken as
 // R.hi + R.lo with v_mfma_f32_16x16x32_f16 (f16 products are exact in f32,
-// f32 accumulation), so the only loss is lo's own rounding, about 2^-22 of |h|.
+// f32 accumulation; the two sums are kept apart and added once at the end), so
+// the only loss is lo's own rounding, about 2^-22 of |h|.
 // Used when every activation is the ONNX default, which keeps |h| within the
 // f16 range (|h| <= max(1, |initial h|)).
 constexpr int kBK16 = 128;           // k chunk (f16 path)
@@ -367,9 +394,9 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
       if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
     }
   }
-  float4 ra[kAPer];
-  h16x8 rb[kBPer];
-  auto fetch = [&](int k0) {
+  float4 ring_a[kPF][kAPer];
+  h16x8 ring_b[kPF][kBPer];
+  auto fetch = [&](int k0, float4* ra, h16x8* rb) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int k = k0 + aoff[i];
@@ -397,7 +424,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
       rb[i] = v;
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const float4* ra, const h16x8* rb) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int q = tid + i * kMThreads;
@@ -421,48 +448,74 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
     }
   };
 
-  const int nbm = BM / 16, nbn = NC / 16, nblk = nbm * nbn;
-  constexpr int kMaxBlk = (BM / 16) * (kMaxNC / 16) / 4 + 1;
-  f32x4 acc[kMaxBlk];
+  // wave w owns column blocks w, w+4 and all row blocks; the hi and lo
+  // products accumulate separately (independent chains) and are added at the end
+  constexpr int NBI = BM / 16;
+  constexpr int CB = kMaxNC / 16 / 4;
+  const int ncb = NC / 16;
+  f32x4 acc_hi[CB][NBI], acc_lo[CB][NBI];
 #pragma unroll
-  for (int q = 0; q < kMaxBlk; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi) acc_hi[cb][bi] = acc_lo[cb][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
   const int nk = (H + kBK16 - 1) / kBK16;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) fetch((kc + 1) * kBK16);
 #pragma unroll
-    for (int q = 0; q < kMaxBlk; ++q) {
-      const int blk = wave + 4 * q;
-      if (blk >= nblk) break;
-      const int bi = blk / nbn, ci = blk - bi * nbn;
-      const int ao = (bi * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4);
-      const int bo = (ci * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4);
+  for (int u = 0; u < kPF; ++u)
+    if (u < nk) fetch(u * kBK16, ring_a[u], ring_b[u]);
+  stash(0, ring_a[0], ring_b[0]);
+  __syncthreads();
+  for (int kc0 = 0; kc0 < nk; kc0 += kPF) {
 #pragma unroll
-      for (int kk = 0; kk < kBK16; kk += 32) {
-        const h16x8 ah = *reinterpret_cast<const h16x8*>(&Ahi[buf][ao + kk]);
-        const h16x8 al = *reinterpret_cast<const h16x8*>(&Alo[buf][ao + kk]);
-        const h16x8 bv = *reinterpret_cast<const h16x8*>(&Bh[buf][bo + kk]);
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, acc[q], 0, 0, 0);
+    for (int u = 0; u < kPF; ++u) {
+      const int kc = kc0 + u;
+      if (kc >= nk) break;
+      const int buf = kc & 1;
+      constexpr int KS = kBK16 / 32;
+      h16x8 ah[NBI][KS], al[NBI][KS];
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int ao = (bi * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4) + 32 * kk;
+          ah[bi][kk] = *reinterpret_cast<const h16x8*>(&Ahi[buf][ao]);
+          al[bi][kk] = *reinterpret_cast<const h16x8*>(&Alo[buf][ao]);
+        }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int ci = wave + 4 * cb;
+        if (ci >= ncb) break;
+        h16x8 bv[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          bv[kk] = *reinterpret_cast<const h16x8*>(&Bh[buf][(ci * 16 + (lane & 15)) * kLDH + 8 * (lane >> 4) + 32 * kk]);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+          for (int bi = 0; bi < NBI; ++bi) {
+            acc_hi[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[bi][kk], bv[kk], acc_hi[cb][bi], 0, 0, 0);
+            acc_lo[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[bi][kk], bv[kk], acc_lo[cb][bi], 0, 0, 0);
+          }
       }
+      const int nx = (u + 1) % kPF;
+      if (kc + 1 < nk) stash(buf ^ 1, ring_a[nx], ring_b[nx]);
+      // slot u held chunk kc, staged an iteration ago: it receives chunk kc + kPF
+      if (kc + kPF < nk) fetch((kc + kPF) * kBK16, ring_a[u], ring_b[u]);
+      __syncthreads();
     }
-    if (kc + 1 < nk) stash(buf ^ 1);
-    __syncthreads();
   }
 
   // accumulator layout of the 16x16 MFMA: element i of lane l is row 4*(l/16) + i, column l%16
   constexpr int LDR = kMaxNC + 1;
 #pragma unroll
-  for (int q = 0; q < kMaxBlk; ++q) {
-    const int blk = wave + 4 * q;
-    if (blk >= nblk) break;
-    const int bi = blk / nbn, ci = blk - bi * nbn;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int ci = wave + 4 * cb;
+    if (ci >= ncb) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc[q][i];
+    for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rec[(bi * 16 + 4 * (lane >> 4) + i) * LDR + ci * 16 + (lane & 15)] = acc_hi[cb][bi][i] + acc_lo[cb][bi][i];
   }
   __syncthreads();
   mfma_epilogue<half_t, BM>(m, rec, len_s, b0, j0, d);

@@ -90,7 +90,7 @@ LARGE = [(c, d, dt) for c in ("LSTM", "GRU", "RNN") for d in ("forward", "bidire
 def test_large_batch_matrix_engine(cell, direction, dtype):
     """Batches of 16 and more take the matrix-core step kernel: ragged batch
     and hidden sizes, every option, both GRU forms, both layouts."""
-    for lbr, layout, B, H in ((0, 0, 37, 50), (1, 1, 70, 33), (0, 1, 16, 130)):
+    for lbr, layout, B, H in ((0, 0, 37, 50), (1, 1, 70, 33), (0, 1, 16, 130), (1, 0, 20, 700)):
         if cell != "GRU" and lbr == 1:
             lbr = 0
         spec = LayerSpec(cell, seq=7, batch=B, input=29, hidden=H, direction=direction, layout=layout,
