@@ -13,27 +13,17 @@
 // the instruction's own order within a chunk), so runs are bit-identical.
 // Operand chunks are staged through LDS, the next chunk is fetched into
 // registers while the current one feeds the matrix cores.
-#include "cells.h"
+#include <cstdio>
+#include <cstdlib>
+
+#include "step_mfma.h"
 
 namespace rnnhip {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kMThreads = 256;
 constexpr int kBK = 64;          // k chunk
 constexpr int kLDA = kBK + 4;    // padded LDS row (floats)
-constexpr int kMaxNC = 128;      // gate rows per tile (Gp * UJ)
 constexpr int kPF = 3;           // k chunks in flight
 constexpr int kSeg = 4;          // elements per load segment (16 bytes of f32 h; 8 bytes of f16 R, 16 of f32 R)
-
-struct MfmaStepArgs {
-  StepArgs a;
-  int UJ;           // units per tile (multiple of 16)
-  int Gp;           // gate blocks computed in this phase
-  int gate_of[4];   // gate block index of each computed block
-  int phase;        // GRU linear_before_reset = 0: 0 = z and r, 1 = candidate; else 0
-  int step;
-};
 
 // Four consecutive elements as f32 (vector load when aligned, else four loads).
 template <bool VEC>
@@ -49,94 +39,6 @@ __device__ __forceinline__ float4 load4(const half_t* p) {
     return make_float4(float(v[0]), float(v[1]), float(v[2]), float(v[3]));
   } else {
     return make_float4(float(p[0]), float(p[1]), float(p[2]), float(p[3]));
-  }
-}
-
-// Gate arithmetic of a finished product tile rec[BM][Gp*UJ] (row stride
-// kMaxNC + 1): one thread per (batch row, unit), in the order of cells.h.
-template <typename T, int BM>
-__device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float* rec, const int* len_s, int b0,
-                                              int j0, int d) {
-  const StepArgs& a = m.a;
-  const int H = a.H, B = a.B, G = a.G, S = a.S;
-  const int s = m.step;
-  const int tid = threadIdx.x;
-  const int UJ = m.UJ;
-  const int64_t DBH = int64_t(a.D) * B * H;
-  const int64_t dBH = int64_t(d) * B * H;
-  constexpr int LDR = kMaxNC + 1;
-  const int GH = G * H;
-  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
-  const Act* acts = a.act + d * a.slots;
-  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
-  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
-  for (int e = tid; e < BM * UJ; e += kMThreads) {
-    const int r = e / UJ, u = e - r * UJ;
-    const int b = b0 + r, j = j0 + u;
-    if (b >= B || j >= H) continue;
-    const int L = len_s[r];
-    if (s >= L) continue;
-    const int t = a.dir_reverse[d] ? (L - 1 - s) : s;
-    const float* xw = a.xw + ((int64_t(d) * S + t) * B + b) * GH;
-    const int64_t sidx = int64_t(b) * H + j;
-    const float* rrow = rec + r * LDR;
-    auto pre = [&](int gi, int g) {
-      const int n = g * H + j;
-      const float wb = bias ? ld(bias, n) : 0.f;
-      const float rbv = bias ? ld(bias, GH + n) : 0.f;
-      return pre_sum(xw[n], rrow[gi * UJ + u], wb, rbv);
-    };
-    if (a.cell == RNN_CELL_LSTM) {
-      float p4[4];
-      p4[0] = pre(0, 0);
-      p4[1] = pre(1, 1);
-      if (a.input_forget) {
-        p4[2] = 0.f;
-        p4[3] = pre(2, 3);
-      } else {
-        p4[2] = pre(2, 2);
-        p4[3] = pre(3, 3);
-      }
-      float peep[3];
-      const float* pp = nullptr;
-      if (a.P) {
-        const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
-        peep[0] = ld(P, j);
-        peep[1] = ld(P, H + j);
-        peep[2] = ld(P, 2 * H + j);
-        pp = peep;
-      }
-      float* cst = a.cell_state + dBH + sidx;
-      float h, c;
-      lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
-      *cst = c;
-      hnext[sidx] = h;
-    } else if (a.cell == RNN_CELL_GRU) {
-      if (a.lbr) {
-        // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
-        const float z = gru_gate(pre(0, 0), a.clip, acts);
-        const float rg = gru_gate(pre(1, 1), a.clip, acts);
-        const int n = 2 * H + j;
-        const float wb = bias ? ld(bias, n) : 0.f;
-        const float rbv = bias ? ld(bias, GH + n) : 0.f;
-        const float ph = (xw[n] + rg * (rrow[2 * UJ + u] + rbv)) + wb;
-        hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
-      } else if (m.phase == 0) {
-        const float z = gru_gate(pre(0, 0), a.clip, acts);
-        const float rg = gru_gate(pre(1, 1), a.clip, acts);
-        a.zbuf[dBH + sidx] = z;
-        a.rhbuf[dBH + sidx] = rg * hprev[sidx];
-      } else {
-        // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
-        const int n = 2 * H + j;
-        const float wb = bias ? ld(bias, n) : 0.f;
-        const float rbv = bias ? ld(bias, GH + n) : 0.f;
-        const float ph = pre_sum(xw[n], rrow[u], wb, rbv);
-        hnext[sidx] = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
-      }
-    } else {
-      hnext[sidx] = rnn_unit(pre(0, 0), a.clip, acts);
-    }
   }
 }
 
@@ -200,7 +102,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
     bptr[i] = nullptr;
     if (q < NC * kSegRow) {
       const int gi = c / UJ, u = c - gi * UJ;
-      if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
+      if (j0 + u < H) bptr[i] = Rd + int64_t(gate_block(m, gi) * H + j0 + u) * H;
     }
   }
   float4 ring_a[kPF][kAPer], ring_b[kPF][kBPer];
@@ -391,7 +293,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
     bptr[i] = nullptr;
     if (q < NC * kBSegRow) {
       const int gi = c / UJ, u = c - gi * UJ;
-      if (j0 + u < H) bptr[i] = Rd + int64_t(m.gate_of[gi] * H + j0 + u) * H;
+      if (j0 + u < H) bptr[i] = Rd + int64_t(gate_block(m, gi) * H + j0 + u) * H;
     }
   }
   float4 ring_a[kPF][kAPer];
@@ -522,8 +424,19 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
 }
 
 // Tile shape (BM batch rows, UJ units): the largest tile that still gives at
-// least 256 workgroups, so every compute unit has work.
+// least 256 workgroups, so every compute unit has work.  RNN_MFMA_TILE=BMxUJ
+// (BM, UJ in 16, 32, 64; Gp*UJ <= 128) overrides the choice, so that tests
+// can reach every tile on small layers.
 void mfma_tile(int B, int H, int D, int Gp, int* bm, int* uj) {
+  if (const char* e = std::getenv("RNN_MFMA_TILE")) {
+    int fb = 0, fu = 0;
+    if (std::sscanf(e, "%dx%d", &fb, &fu) == 2 && (fb == 16 || fb == 32 || fb == 64) &&
+        (fu == 16 || fu == 32 || fu == 64) && Gp * fu <= kMaxNC) {
+      *bm = fb;
+      *uj = fu;
+      return;
+    }
+  }
   static const int cand[][2] = {{64, 64}, {64, 32}, {32, 32}, {32, 16}, {16, 16}};
   for (const auto& c : cand) {
     if (Gp * c[1] > kMaxNC) continue;
@@ -581,7 +494,10 @@ hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipSt
     mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
     m.UJ = uj;
     hipError_t e;
-    if (a.dtype == RNN_DTYPE_F16 && p.def_acts) {
+    const bool h16 = a.dtype == RNN_DTYPE_F16 && p.def_acts;
+    if ((h16 || a.dtype == RNN_DTYPE_F32) && step_dma_supported(a, h16)) {
+      e = launch_step_dma(m, bm, h16, s);
+    } else if (h16) {
       e = bm == 64 ? launch_h16<64>(m, a.H, a.B, a.D, s)
                    : bm == 32 ? launch_h16<32>(m, a.H, a.B, a.D, s) : launch_h16<16>(m, a.H, a.B, a.D, s);
     } else if (a.dtype == RNN_DTYPE_F32) {

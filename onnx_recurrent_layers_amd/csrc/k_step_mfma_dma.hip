@@ -1,0 +1,615 @@
+// k_step_mfma_dma.hip -- the matrix-core step (stage 3 of a layer,
+// "Recurrent layers" page, "How a layer runs", item 3) for hidden sizes that
+// are whole 16-byte segments: h rows and R rows go from global memory straight
+// into LDS with buffer loads carrying the LDS bit, several k chunks ahead of
+// the matrix cores, so no register staging and no per-element bounds branches.
+//
+// Tile and arithmetic are those of the other matrix-core step: a workgroup
+// owns BM batch rows x UJ units of one direction with all Gp gate blocks of
+// those units (product tile [BM] x [Gp*UJ], K = H), and finishes the gate
+// arithmetic itself.  Two modes:
+//   mode 0, f32 tensors: v_mfma_f32_16x16x4_f32 on f32 h and f32 R;
+//   mode 1, f16 tensors with the default activations: h split into
+//     hi = f16(h) and lo = f16(h - hi), R.hi + R.lo on v_mfma_f32_16x16x32_f16
+//     with separate f32 accumulators (f16 products are exact in f32).
+// The k order is fixed (chunks in increasing order, a fixed order within a
+// chunk), so runs are bit-identical.
+//
+// Loads: one buffer resource per operand (h of this direction, R of this
+// direction).  A segment that lies outside the tile (rows past the batch or
+// the tile's gate rows, k past H) gets an offset beyond the resource's size,
+// which the hardware answers with zeros and no memory traffic.  Each wave
+// issues the same number of loads per chunk, so the wait for a chunk is a
+// fixed vector-memory count.
+//
+// LDS layout of a chunk: rows of 16-byte segments, unpadded; the segment of
+// logical index s of row r is stored at slot s ^ (r & 15), so that the 16
+// rows a matrix-core operand read touches land in 16 different bank groups.
+// The k index is permuted inside a chunk (lane group q of an operand takes a
+// contiguous quarter of the chunk), identically for h and R, so each lane
+// reads whole 16-byte segments; a sum over a permuted k range is the same sum.
+#include "step_mfma.h"
+
+namespace rnnhip {
+
+typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
+
+#define RNN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define RNN_GLOBAL_PTR(p) ((__attribute__((address_space(1))) void*)(const_cast<float*>(p)))
+
+constexpr unsigned kOutOfRange = 0x80000000u;   // beyond every resource size used here
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kLdsBudget = 144 * 1024;          // staging bytes per workgroup
+
+// s_waitcnt immediate of the gfx9 encoding: vector-memory count vm (6 bits,
+// split), export count left open, LDS count lgkm.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Wait until at most VM of this wave's vector-memory loads are outstanding and
+// its LDS accesses are done, then meet the other waves.  The empty asm
+// statements keep the compiler from moving memory accesses across.
+template <int VM>
+__device__ __forceinline__ void chunk_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MODE> struct DmaGeo;
+template <> struct DmaGeo<0> {           // f32 h, f32 R
+  typedef float RT;
+  static constexpr int KC = 64;          // k per chunk
+  static constexpr int ASEGS = 16;       // 16-byte segments per h row of a chunk
+  static constexpr int BELEMS = 4;       // R elements per segment
+};
+template <> struct DmaGeo<1> {           // f32 h split on the fly, f16 R
+  typedef half_t RT;
+  static constexpr int KC = 128;
+  static constexpr int ASEGS = 32;
+  static constexpr int BELEMS = 8;
+};
+
+template <int MODE, int BM, int CB>
+struct DmaCfg {
+  typedef DmaGeo<MODE> Geo;
+  static constexpr int A_BYTES = BM * Geo::ASEGS * 16;
+  static constexpr int B_BYTES = CB * 4 * 16 * 256;           // 16 rows x 16 segments per column block
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int REC = BM * (kMaxNC + 1) * 4;             // product tile, over slot 0
+  static constexpr int NS0 = (kLdsBudget - (REC > STAGE ? REC - STAGE : 0)) / STAGE;
+  static constexpr int NS = NS0 > 4 ? 4 : NS0;                  // chunks resident (NS - 1 in flight)
+  static constexpr int LA = A_BYTES / 1024 / 4;                 // h loads per wave per chunk
+  static constexpr int LB = 4 * CB;                             // R loads per wave per chunk
+  static constexpr int L = LA + LB;
+  static_assert(NS >= 2, "two chunks must fit in LDS");
+  static_assert((A_BYTES / 1024) % 4 == 0, "h loads must split evenly over the four waves");
+  static_assert((NS - 2) * L < 64, "wait count must fit the counter");
+};
+
+// Operands of the gate arithmetic of one (batch row, unit) element besides
+// its recurrent products.  They do not depend on the product, so the first
+// element of each thread is gathered before the k loop and its loads overlap
+// the matrix work.
+struct EpiIn {
+  float xv[4];     // Xw of the computed gate blocks
+  unsigned wb[4];  // Wb of those blocks as loaded (0 without B); widened at use,
+  unsigned rb[4];  //   so that waiting for the loads is left to the arithmetic
+  unsigned pp[3];  // P_i, P_o, P_f (LSTM), likewise
+  float cprev;     // LSTM cell state
+  float hprev;     // GRU previous hidden state
+  float z;         // GRU linear_before_reset = 0, second pass: z of the first
+  bool live;       // the element exists and its row still runs at this step
+};
+
+// Everything the gate arithmetic of one direction needs, read out of the
+// launch arguments once at the start (uniform values).  The arithmetic then
+// touches the argument block nowhere: when many inlined copies of it index
+// the block, the compiler stops reading the block in place and copies it to
+// scratch memory.
+struct EpiCtx {
+  __amdgpu_buffer_rsrc_t bias, peep;   // absent vector: size 0, loads return zeros without traffic
+  const float* xw;      // this direction's Xw, [S][B][G*H]
+  const float* hprev;   // h of this step, [B][H]
+  float* hnext;         // h of the next step, [B][H]
+  float* cst;           // LSTM cell state, [B][H]
+  float* zbuf;          // GRU z of the first pass, [B][H]
+  float* rhbuf;         // GRU r*h, [B][H]
+  float clip;
+  int H, B, GH, s, cell, lbr, phase, input_forget, has_p, rev, Gp;
+  int gate[4];
+  Act act[3];
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+template <typename RT>
+__device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
+  const StepArgs& a = m.a;
+  EpiCtx c;
+  c.H = a.H;
+  c.B = a.B;
+  c.GH = a.G * a.H;
+  c.s = m.step;
+  c.cell = a.cell;
+  c.lbr = a.lbr;
+  c.phase = m.phase;
+  c.input_forget = a.input_forget;
+  c.has_p = a.P != nullptr;
+  c.rev = uniform(a.dir_reverse[d]);
+  c.Gp = m.Gp;
+  c.clip = a.clip;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c.gate[k] = uniform(m.gate_of[k]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int i = d * a.slots + (k < a.slots ? k : 0);
+    c.act[k].kind = uniform(a.act[i].kind);
+    c.act[k].alpha = uniform(a.act[i].alpha);
+    c.act[k].beta = uniform(a.act[i].beta);
+  }
+  const int64_t DBH = int64_t(a.D) * a.B * a.H, dBH = int64_t(d) * a.B * a.H;
+  c.xw = a.xw + int64_t(d) * a.S * a.B * c.GH;
+  c.hprev = a.slab + int64_t(m.step) * DBH + dBH;
+  c.hnext = a.slab + int64_t(m.step + 1) * DBH + dBH;
+  c.cst = a.cell_state + dBH;
+  c.zbuf = a.zbuf + dBH;
+  c.rhbuf = a.rhbuf + dBH;
+  const RT* bias = a.bias ? static_cast<const RT*>(a.bias) + int64_t(d) * 2 * c.GH : nullptr;
+  const RT* P = a.P ? static_cast<const RT*>(a.P) + int64_t(d) * 3 * a.H : nullptr;
+  c.bias = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(bias), 0, bias ? 2 * c.GH * int(sizeof(RT)) : 0, kRsrcWord3);
+  c.peep = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(P), 0, P ? 3 * a.H * int(sizeof(RT)) : 0, kRsrcWord3);
+  return c;
+}
+
+// f16 elements are loaded as the aligned dword that holds them (the vectors
+// have an even length), so that no conversion sits at the load; widen() picks
+// the half by the parity of the element index.
+template <typename RT>
+__device__ __forceinline__ unsigned res_load(__amdgpu_buffer_rsrc_t r, int idx) {
+  if constexpr (sizeof(RT) == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, (idx * 2) & ~3, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0);
+}
+
+template <typename RT>
+__device__ __forceinline__ float widen(unsigned v, int odd) {
+  if constexpr (sizeof(RT) == 2) return float(__builtin_bit_cast(half_t, (unsigned short)(v >> (odd * 16))));
+  else return __builtin_bit_cast(float, v);
+}
+
+// Element e of the tile is row e >> ujs, unit e & (UJ - 1); elements from
+// n_el on do not exist.
+template <typename RT>
+__device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, int e, int n_el, int ujs, int b0, int j0,
+                                           EpiIn& o) {
+  const int H = c.H, s = c.s;
+  const int r = e >> ujs, u = e & ((1 << ujs) - 1);
+  const int b = b0 + r, j = j0 + u;
+  const int L = e < n_el ? len_s[r] : 0;
+  o.live = b < c.B && j < H && s < L;
+  if (j >= H) return;
+  // the unit's biases and peepholes, also for a row that does not run: the
+  // thread's later elements (same unit) take them from here
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    if (gi >= c.Gp) break;
+    const int n = c.gate[gi] * H + j;
+    o.wb[gi] = res_load<RT>(c.bias, n);
+    o.rb[gi] = res_load<RT>(c.bias, c.GH + n);
+  }
+  if (c.cell == RNN_CELL_LSTM) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) o.pp[k] = res_load<RT>(c.peep, k * H + j);
+  }
+  if (!o.live) return;
+  const int t = c.rev ? (L - 1 - s) : s;
+  const float* xw = c.xw + (int64_t(t) * c.B + b) * c.GH;
+  const int64_t si = int64_t(b) * H + j;
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    if (gi >= c.Gp) break;
+    o.xv[gi] = xw[c.gate[gi] * H + j];
+  }
+  if (c.cell == RNN_CELL_LSTM) {
+    o.cprev = c.cst[si];
+  } else if (c.cell == RNN_CELL_GRU) {
+    o.hprev = c.hprev[si];
+    if (!c.lbr && c.phase == 1) o.z = c.zbuf[si];
+  }
+}
+
+// Gate arithmetic of one gathered element with its products rrow[gi*UJ + u],
+// in the order of cells.h.
+template <typename RT, bool DEF>
+__device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, const float* rec, int e, int ujs, int b0,
+                                           int j0) {
+  if (!o.live) return;
+  constexpr int LDR = kMaxNC + 1;
+  const int UJ = 1 << ujs;
+  const int r = e >> ujs, u = e & (UJ - 1);
+  const int b = b0 + r, j = j0 + u;
+  const int64_t si = int64_t(b) * c.H + j;
+  const float* rrow = rec + r * LDR + u;
+  const Act* acts = c.act;
+  const int odd = j & 1;   // every bias and peephole index of unit j has the parity of j (H is even)
+  auto pre = [&](int gi) {
+    return pre_sum(o.xv[gi], rrow[gi * UJ], widen<RT>(o.wb[gi], odd), widen<RT>(o.rb[gi], odd));
+  };
+  if (c.cell == RNN_CELL_LSTM) {
+    float p4[4];
+    p4[0] = pre(0);
+    p4[1] = pre(1);
+    if (c.input_forget) {            // computed blocks i, o, c
+      p4[2] = 0.f;
+      p4[3] = pre(2);
+    } else {
+      p4[2] = pre(2);
+      p4[3] = pre(3);
+    }
+    float h, cc;
+    const float pp[3] = {widen<RT>(o.pp[0], odd), widen<RT>(o.pp[1], odd), widen<RT>(o.pp[2], odd)};
+    if (c.has_p)   // two calls, so that the peephole array stays in registers
+      lstm_unit<DEF>(p4, pp, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
+    else
+      lstm_unit<DEF>(p4, nullptr, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
+    c.cst[si] = cc;
+    c.hnext[si] = h;
+  } else if (c.cell == RNN_CELL_GRU) {
+    if (c.lbr) {
+      // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+      const float z = gru_gate<DEF>(pre(0), c.clip, acts);
+      const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
+      const float ph = (o.xv[2] + rg * (rrow[2 * UJ] + widen<RT>(o.rb[2], odd))) + widen<RT>(o.wb[2], odd);
+      c.hnext[si] = gru_unit<DEF>(z, ph, o.hprev, c.clip, acts);
+    } else if (c.phase == 0) {
+      const float z = gru_gate<DEF>(pre(0), c.clip, acts);
+      const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
+      c.zbuf[si] = z;
+      c.rhbuf[si] = rg * o.hprev;
+    } else {
+      // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
+      c.hnext[si] = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
+    }
+  } else {
+    c.hnext[si] = rnn_unit<DEF>(pre(0), c.clip, acts);
+  }
+}
+
+// Per-element planes of the elements after each thread's first: Xw of the Gp
+// computed blocks, then the state the cell reads (LSTM c, GRU h), then the
+// GRU z of the first pass.  Each plane holds n_el floats, element e at e.
+__host__ __device__ constexpr int epi_state_planes(int cell, int lbr, int phase) {
+  return cell == RNN_CELL_LSTM ? 1 : cell == RNN_CELL_GRU ? 1 + (!lbr && phase == 1) : 0;
+}
+
+// Load the planes of elements tid + k*256, k = 1..E-1, straight into LDS
+// (every load in flight at once, no registers).  Lane l of a wave writes 4
+// bytes at its instruction's base + 4*l, which is element e's slot since the
+// wave's 64 elements are consecutive.  Elements that do not run load a valid
+// dummy address.
+__device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s, float* planes, int n_el, int ujs,
+                                               int b0, int j0) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int E = n_el / kMThreads;
+  const int j = j0 + (tid & ((1 << ujs) - 1));   // the same unit for every element of this thread
+  const int ns = epi_state_planes(c.cell, c.lbr, c.phase);
+  for (int k = 1; k < E; ++k) {
+    const int e = tid + k * kMThreads;
+    const int r = e >> ujs, b = b0 + r;
+    const int L = len_s[r];
+    const bool live = b < c.B && j < c.H && c.s < L;
+    const int t = live ? (c.rev ? L - 1 - c.s : c.s) : 0;
+    const int64_t row = live ? (int64_t(t) * c.B + b) * c.GH + j : 0;
+    const int64_t si = live ? int64_t(b) * c.H + j : 0;
+    float* dst = planes + k * kMThreads + wave * 64;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)   // fixed indices keep the context in registers
+      if (gi < c.Gp)
+        __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(c.xw + row + (live ? c.gate[gi] * c.H : 0)),
+                                         RNN_LDS_PTR(dst + gi * n_el), 4, 0, 0);
+    if (ns > 0) {
+      const float* st = c.cell == RNN_CELL_LSTM ? c.cst : c.hprev;
+      __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(st + si), RNN_LDS_PTR(dst + c.Gp * n_el), 4, 0, 0);
+    }
+    if (ns > 1)
+      __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(c.zbuf + si), RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 4, 0, 0);
+  }
+}
+
+// Gate arithmetic of elements k = 1..E-1 from the planes; biases and
+// peepholes are those of the thread's first element (same unit).
+template <typename RT, bool DEF>
+__device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& first, const int* len_s, const float* rec,
+                                                const float* planes, int n_el, int ujs, int b0, int j0) {
+  const int tid = threadIdx.x;
+  const int E = n_el / kMThreads;
+  const int j = j0 + (tid & ((1 << ujs) - 1));
+  for (int k = 1; k < E; ++k) {
+    const int e = tid + k * kMThreads;
+    const int r = e >> ujs, b = b0 + r;
+    EpiIn o = first;
+    o.live = b < c.B && j < c.H && c.s < len_s[r];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+      if (gi < c.Gp) o.xv[gi] = planes[gi * n_el + e];
+    const float sv = planes[c.Gp * n_el + e];
+    o.cprev = sv;
+    o.hprev = sv;
+    o.z = planes[(c.Gp + 1) * n_el + e];
+    epi_finish<RT, DEF>(c, o, rec, e, ujs, b0, j0);
+  }
+}
+
+template <int MODE, int BM, int CB>
+__global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
+  typedef DmaCfg<MODE, BM, CB> C;
+  typedef typename C::Geo Geo;
+  typedef typename Geo::RT RT;
+  constexpr int KC = Geo::KC, ASEGS = Geo::ASEGS, BELEMS = Geo::BELEMS;
+  constexpr int NS = C::NS, L = C::L, LA = C::LA;
+  constexpr int NBI = BM / 16;
+  // one LDS object per resident chunk: the compiler then tells the loads
+  // into one chunk from the reads of another and waits only for the former
+  constexpr int REC_BYTES = BM * (kMaxNC + 1) * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[C::STAGE > REC_BYTES ? C::STAGE : REC_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[NS > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[NS > 3 ? C::STAGE : 16];
+  __shared__ int len_s[BM];
+  __shared__ int any_s;
+
+  const StepArgs& a = m.a;
+  const int H = a.H, B = a.B, G = a.G, S = a.S;
+  const int s = m.step;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = blockIdx.x * m.UJ;
+  const int b0 = blockIdx.y * BM;
+  const int d = blockIdx.z;
+  const int UJ = m.UJ, ncb = (m.Gp * UJ) >> 4;
+  const int ujs = __builtin_ctz(unsigned(UJ));   // UJ is a power of two
+
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const RT* Rd = static_cast<const RT*>(a.R) + int64_t(d) * G * H * H;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<RT*>(Rd), 0, int(unsigned(G) * unsigned(H) * unsigned(H) * unsigned(sizeof(RT))), kRsrcWord3);
+
+  // h segments of this lane: load i of the wave fills LDS bytes
+  // [(wave*LA + i) * 1024, +1024) of the chunk, lane l the 16 bytes at 16*l
+  unsigned arow[LA];
+  int aseg[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int p = (wave * LA + i) * 64 + lane;
+    const int r = p / ASEGS;
+    aseg[i] = (p % ASEGS) ^ (r & 15);
+    arow[i] = b0 + r < B ? unsigned(b0 + r) * unsigned(H) * 4u : kOutOfRange;
+  }
+  // R segments: wave w owns column blocks w and w + 4 (CB of them); load i of
+  // a block fills its rows 4i..4i+3
+  unsigned brow[CB][4];
+  const int bseg0 = lane & 15;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = wave + 4 * cb;
+      const int c = ci * 16 + 4 * i + (lane >> 4);
+      const int gi = c >> ujs, u = c & (UJ - 1);
+      const bool ok = ci < ncb && j0 + u < H;
+      brow[cb][i] = ok ? unsigned(gate_block(m, gi) * H + j0 + u) * unsigned(H) * unsigned(sizeof(RT)) : kOutOfRange;
+    }
+  auto slot = [&](int i) -> unsigned char* { return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3; };
+  auto fetch = [&](int kc, unsigned char* st) {
+    const int k0 = kc * KC;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int k = k0 + aseg[i] * 4;
+      // a row outside the tile starts at the out-of-range marker, so row + k stays out of range
+      const unsigned off = k < H ? arow[i] + unsigned(k) * 4u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, RNN_LDS_PTR(st + (wave * LA + i) * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const int k = k0 + (bseg0 ^ rr) * BELEMS;
+        const unsigned off = k < H ? brow[cb][i] + unsigned(k) * unsigned(sizeof(RT)) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, RNN_LDS_PTR(st + C::A_BYTES + ((wave + 4 * cb) * 16 + 4 * i) * 256), 16, off, 0, 0, 0);
+      }
+  };
+
+  // lengths of the tile's rows (wave 0); the load overlaps the first chunks
+  int lv = 0;
+  if (wave == 0 && lane < BM && b0 + lane < B) lv = a.lens ? a.lens[b0 + lane] : S;
+
+  const int nk = (H + KC - 1) / KC;
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c) fetch(c, slot(c));
+
+  if (wave == 0) {
+    const int L_ = lv < 0 ? 0 : (lv > S ? S : lv);
+    const int Lr = L_ < a.steps ? L_ : a.steps;
+    if (lane < BM) len_s[lane] = Lr;
+    const unsigned long long live = __ballot(lane < BM && s < Lr);
+    if (lane == 0) any_s = live != 0ull;
+  }
+
+  const int q = lane >> 4, r16 = lane & 15;
+  f32x4 acc[CB][NBI];
+  f32x4 acc_lo[MODE == 1 ? CB : 1][MODE == 1 ? NBI : 1];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi) acc[cb][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE == 1) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi) acc_lo[cb][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  chunk_barrier<(NS - 1) * L>();      // the lengths are visible
+  if (!any_s) {                       // every row of the tile has ended
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    return;
+  }
+  const EpiCtx ctx = epi_context<RT>(m, d);
+  const int n_el = BM * UJ;   // a multiple of the workgroup size
+  EpiIn first;
+  epi_gather<RT>(ctx, len_s, tid, n_el, ujs, b0, j0, first);
+
+  // chunk kc lives in slot kc % NS; the loop is unrolled over the slots so
+  // that every slot is a fixed LDS object.  The chunk count is rounded up to
+  // whole rounds of NS: chunks past the end hold zeros and add nothing.
+  for (int kc0 = 0; kc0 < nk; kc0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+    const int kc = kc0 + u;
+    chunk_barrier<(NS - 2) * L>();   // chunk kc has landed for every wave; chunk kc - 1 is read
+    fetch(kc + NS - 1, slot((u + NS - 1) % NS));   // the slot chunk kc - 1 used; past the end: zeros
+    const unsigned char* st = slot(u);
+    const unsigned char* Bs = st + C::A_BYTES;
+    if constexpr (MODE == 0) {
+      // operands are read as whole vectors (a split read loses the LDS
+      // object the compiler needs to keep its waits narrow)
+      f32x4 bq[CB][4];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bq[cb][j] = *reinterpret_cast<const f32x4*>(
+              Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * q + j) ^ r16) << 4));
+      f32x4 aq[NBI][4];
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          aq[bi][j] = *reinterpret_cast<const f32x4*>(st + (bi * 16 + r16) * 256 + (((4 * q + j) ^ r16) << 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int bi = 0; bi < NBI; ++bi)
+              acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[bi][j][e], bq[cb][j][e], acc[cb][bi], 0, 0, 0);
+    } else {
+      hx8 bv[CB][4];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          bv[cb][kk] =
+              *reinterpret_cast<const hx8*>(Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * q + kk) ^ r16) << 4));
+      hx8 ah[NBI][4], al[NBI][4];
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const unsigned char* row = st + (bi * 16 + r16) * 512;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(row + (((8 * q + 2 * kk) ^ r16) << 4));
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(row + (((8 * q + 2 * kk + 1) ^ r16) << 4));
+          const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int z = 0; z < 8; ++z) {
+            const half_t hi = half_t(x[z]);
+            ah[bi][kk][z] = hi;
+            al[bi][kk][z] = half_t(x[z] - float(hi));
+          }
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int bi = 0; bi < NBI; ++bi) {
+            acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[bi][kk], bv[cb][kk], acc[cb][bi], 0, 0, 0);
+            acc_lo[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[bi][kk], bv[cb][kk], acc_lo[cb][bi], 0, 0, 0);
+          }
+    }
+    }
+  }
+  // the loads past the last chunk still write LDS: let them land before reuse
+  chunk_barrier<0>();
+
+  // accumulator layout of the 16x16 products: element i of lane l is row
+  // 4*(l/16) + i, column l%16; column blocks past the tile are dropped
+  float* rec = reinterpret_cast<float*>(st0);
+  constexpr int LDR = kMaxNC + 1;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int ci = wave + 4 * cb;
+    if (ci >= ncb) break;
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[cb][bi][i];
+        if constexpr (MODE == 1) v += acc_lo[cb][bi][i];
+        rec[(bi * 16 + 4 * q + i) * LDR + ci * 16 + r16] = v;
+      }
+  }
+  __syncthreads();
+
+  // gate arithmetic: the first element from its early gather; the others
+  // from planes loaded into slot 1 (the host picks a column split whose
+  // slot holds them), all loads in flight together
+  constexpr bool DEF = MODE == 1;
+  float* planes = reinterpret_cast<float*>(st1);
+  if (n_el > kMThreads) epi_tile_issue(ctx, len_s, planes, n_el, ujs, b0, j0);
+  epi_finish<RT, DEF>(ctx, first, rec, tid, ujs, b0, j0);
+  if (n_el > kMThreads) {
+    __syncthreads();   // waits for this wave's loads, then for the other waves
+    epi_tile_finish<RT, DEF>(ctx, first, len_s, rec, planes, n_el, ujs, b0, j0);
+  }
+}
+
+template <int MODE, int BM, int CB>
+static hipError_t launch_cfg(const MfmaStepArgs& m, hipStream_t s) {
+  const StepArgs& a = m.a;
+  const dim3 grid(unsigned((a.H + m.UJ - 1) / m.UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((step_dma_kernel<MODE, BM, CB>), grid, dim3(kMThreads), 0, s, m);
+  return hipGetLastError();
+}
+
+// Column split: one 16-column block per wave when the tile has at most four,
+// else two; two also when slot 1 of the one-block layout cannot hold the
+// epilogue planes.
+template <int MODE, int BM>
+static hipError_t launch_bm(const MfmaStepArgs& m, hipStream_t s) {
+  const int ncb = (m.Gp * m.UJ) >> 4;
+  const int planes = (m.Gp + epi_state_planes(m.a.cell, m.a.lbr, m.phase)) * BM * m.UJ * 4;
+  if (ncb <= 4 && planes <= DmaCfg<MODE, BM, 1>::STAGE) return launch_cfg<MODE, BM, 1>(m, s);
+  if (planes > DmaCfg<MODE, BM, 2>::STAGE) return hipErrorInvalidValue;
+  return launch_cfg<MODE, BM, 2>(m, s);
+}
+
+bool step_dma_supported(const StepArgs& a, bool h16) {
+  const int seg = h16 ? 8 : 4;   // elements of a 16-byte segment of R
+  const uint64_t esize = h16 ? 2 : 4;
+  if (a.H % seg != 0 || reinterpret_cast<uintptr_t>(a.R) % 16 != 0) return false;
+  // every offset, and the out-of-range marker above them, fits 32 bits
+  if (uint64_t(a.G) * a.H * a.H * esize >= kOutOfRange) return false;
+  if (uint64_t(a.B) * a.H * 4 >= kOutOfRange) return false;
+  return true;
+}
+
+hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, bool h16, hipStream_t s) {
+  if (h16)
+    return bm == 64 ? launch_bm<1, 64>(m, s) : bm == 32 ? launch_bm<1, 32>(m, s) : launch_bm<1, 16>(m, s);
+  return bm == 64 ? launch_bm<0, 64>(m, s) : bm == 32 ? launch_bm<0, 32>(m, s) : launch_bm<0, 16>(m, s);
+}
+
+}  // namespace rnnhip

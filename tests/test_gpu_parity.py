@@ -102,6 +102,38 @@ def test_large_batch_matrix_engine(cell, direction, dtype):
         check(spec, inp, engine="launch", what=f"large {cell}/{direction}/{dtype}/lbr{lbr}/L{layout}/B{B}/H{H}")
 
 
+# Layers whose rows are whole 16-byte segments take the direct-to-LDS
+# matrix-core step; RNN_MFMA_TILE forces each tile shape (and with it the
+# one- or two-block column split) on small layers.  Hidden sizes leave a
+# partial last k chunk and a partial last unit tile; batches leave empty rows.
+DMA_CASES = [
+    # cell, dtype, direction, layout, option, B, H, tile
+    ("LSTM", "f32", "bidirectional", 0, 0, 37, 64, "16x16"),
+    ("LSTM", "f32", "forward", 1, 0, 37, 72, "64x32"),
+    ("LSTM", "f16", "bidirectional", 1, 1, 33, 264, "32x32"),
+    ("LSTM", "f16", "reverse", 0, 0, 40, 136, "16x32"),
+    ("GRU", "f16", "bidirectional", 0, 0, 70, 136, "64x32"),
+    ("GRU", "f32", "reverse", 0, 1, 20, 256, "32x16"),
+    ("GRU", "f32", "forward", 1, 0, 17, 96, "64x16"),
+    ("RNN", "f32", "bidirectional", 0, 0, 20, 520, "64x64"),
+    ("RNN", "f16", "forward", 1, 0, 64, 128, "64x64"),
+    ("GRU", "f16", "forward", 0, 1, 16, 1024, None),
+]
+
+
+@pytest.mark.parametrize("cell,dtype,direction,layout,opt,B,H,tile", DMA_CASES,
+                         ids=["-".join(map(str, c)) for c in DMA_CASES])
+def test_matrix_step_direct_to_lds(cell, dtype, direction, layout, opt, B, H, tile, monkeypatch):
+    if tile:
+        monkeypatch.setenv("RNN_MFMA_TILE", tile)
+    spec = LayerSpec(cell, seq=6, batch=B, input=24, hidden=H, direction=direction, layout=layout, dtype=dtype,
+                     linear_before_reset=opt if cell == "GRU" else 0,
+                     input_forget=opt if cell == "LSTM" else 0, init_h=True, init_c=cell == "LSTM",
+                     lens=True, peephole=cell == "LSTM", clip=2.0, outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 31, Dists(sequence_lens=("I", 0, 6), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    check(spec, inp, engine="launch", what=f"lds-direct {cell}/{dtype}/{direction}/L{layout}/opt{opt}/B{B}/H{H}/{tile}")
+
+
 def test_large_batch_general_activations():
     """The matrix-core step kernel with non-default activations (f16 tensors
     then take the f32 path, f32 tensors always do)."""
