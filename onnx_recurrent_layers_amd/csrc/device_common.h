@@ -7,6 +7,10 @@
 
 #include "plan.h"
 
+// Address-space casts for the loads that write LDS directly.
+#define RNN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define RNN_GLOBAL_PTR(p) ((__attribute__((address_space(1))) void*)(const_cast<float*>(p)))
+
 namespace rnnhip {
 
 typedef _Float16 half_t;

@@ -34,8 +34,6 @@ namespace rnnhip {
 
 typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
 
-#define RNN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-#define RNN_GLOBAL_PTR(p) ((__attribute__((address_space(1))) void*)(const_cast<float*>(p)))
 
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond every resource size used here
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
