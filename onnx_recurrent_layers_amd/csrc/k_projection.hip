@@ -202,9 +202,16 @@ static hipError_t launch_tile(const ProjArgs& a, const SetupArgs& sa, int setup_
   return hipGetLastError();
 }
 
+hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s);
+
 hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s) {
   const int64_t n_state = int64_t(sa.D) * sa.B * sa.H;
   const int setup_blocks = n_state > 0 ? int(std::min<int64_t>((n_state + 255) / 256, 1024)) : 0;
+  // large f16 layers: 256x256 tiles loaded straight into LDS (k_projection_lds.hip)
+  if (dtype == RNN_DTYPE_F16 && a.M > 0 && a.N > 0) {
+    const hipError_t e = launch_projection_lds(a, sa, setup_blocks, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   // 128x128 tiles when they still give every compute unit a workgroup, else 64x64
   const int64_t big = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.D;
   const bool use_big = big >= 256;

@@ -56,6 +56,36 @@ def test_projection_scratch(dtype, layout):
         assert err <= 1e-4, (d, err)
 
 
+@pytest.mark.parametrize("layout,cell,input_forget,S,B,I,H", [
+    (0, "LSTM", 0, 13, 11, 72, 40),      # ragged M, N and K tails, several tiles
+    (1, "LSTM", 1, 9, 70, 136, 256),     # skipped f block of whole tiles, layout 1
+    (1, "GRU", 0, 33, 17, 264, 96),
+    (0, "RNN", 0, 40, 20, 520, 300),
+])
+def test_projection_lds_tiles(layout, cell, input_forget, S, B, I, H, monkeypatch):
+    """The 256x256 f16 projection loaded straight into LDS, forced onto small
+    layers, against the oracle's plain product."""
+    import torch
+    monkeypatch.setenv("RNN_PROJ_LDS_MIN_TILES", "1")
+    spec = LayerSpec(cell, seq=S, batch=B, input=I, hidden=H, layout=layout, dtype="f16", input_forget=input_forget,
+                     direction="bidirectional", outputs=("Y_h",))
+    inp = make_inputs(spec, 7)
+    note(f"case projection-lds {cell} L{layout} S{S} B{B} I{I} H{H}")
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    D, G = 2, spec.gates
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
+    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
+    A = X.reshape(S * B, I)
+    for d in range(D):
+        ref = oracle.projection(A, inp["W"][d])
+        cols = np.ones(G * H, bool)
+        if input_forget:
+            cols[2 * H:3 * H] = False     # the f block is not computed
+        err = np.max(np.abs(xw[d][:, cols].astype(np.float64) - ref[:, cols]))
+        assert err <= 1e-3, (d, err)
+
+
 # ---------------------------------------------------------------------------
 # the page's test matrix on small shapes that span several tiles and a ragged tail
 # ---------------------------------------------------------------------------
