@@ -59,10 +59,13 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-# Measured HBM traffic of the persistent step kernel on the default workload,
-# from two rocprofv3 counter runs (see the profile file); it is reported only
-# while the kernel sources still hash to what was profiled.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "persistent_step_bilstm_s80_b1_h256_f32.md")
+# Measured HBM traffic per launch of the step kernel on a workload, from two
+# rocprofv3 counter runs (see each profile file); it is reported only while
+# the kernel sources still hash to what was profiled.
+TRAFFIC_PROFILES = {
+    ("C2", "persistent"): os.path.join(ROOT, "profiles", "persistent_step_bilstm_s80_b1_h256_f32.md"),
+    ("C4", "launch"): os.path.join(ROOT, "profiles", "mfma_step_lstm_s256_b64_h1024_f16.md"),
+}
 
 
 def profiled_traffic(path: str):
@@ -207,8 +210,8 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "kernel": "recurrent step", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-            "traffic": (profiled_traffic(TRAFFIC_PROFILE)
-                        if (args.config == "C2" and engine_name == "persistent") else None),
+            "traffic": (profiled_traffic(TRAFFIC_PROFILES[(args.config, engine_name)])
+                        if (args.config, engine_name) in TRAFFIC_PROFILES else None),
             "bytes_per_launch": int(bytes_per_launch), "launch_us": round(launch_ms * 1000.0, 3),
             "launches_per_layer": step_launches,
         },

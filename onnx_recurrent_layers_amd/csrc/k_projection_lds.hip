@@ -51,6 +51,8 @@ __device__ __forceinline__ void chunk_barrier() {
   asm volatile("" ::: "memory");
 }
 
+}  // namespace
+
 struct TileMap {
   int mt, nct, tiles_per_dir, per_xcd, sb0, nskip;
 };
@@ -173,8 +175,6 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
         if (m < a.M && n < a.N) out[m * a.N + n] = acc[i][j][e];
       }
 }
-
-}  // namespace
 
 // Takes the layer when the operands are f16 rows of whole 16-byte segments,
 // every byte offset fits 32 bits and the tiles fill the chip; otherwise
