@@ -63,12 +63,16 @@ __device__ __forceinline__ void put_word(unsigned long long* p, unsigned tag, fl
 }
 
 // Copy the words of step `tag` of every active batch row of one direction
-// (src: [B][H]) into hs[k][NB], waiting for each word to carry the tag.  A
-// thread keeps up to kChunk loads in flight and re-polls only stale words.
+// (src: [B][H]) into the workgroup's copy of h, waiting for each word to carry
+// the tag.  That copy is hs[k][NB] in f32 for the vector-ALU products, or two
+// f16 planes [NB][HS] (hi = f16(h), lo = f16(h - hi)) for the matrix-core
+// products.  A thread keeps up to kChunk loads in flight and re-polls only
+// stale words.
 // issue() sends the first loads; complete() waits.  Memory operations issued
 // between the two (output stores, the projection prefetch) are not waited for:
 // the load counter retires in order, so only earlier operations delay a wait.
 constexpr int kChunk = 24;
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left open
 constexpr int kPollThreads = kPThreads - 64;  // waves 1..3 poll; wave 0 computes gates and does the other memory traffic
 
 struct WordPoll {
@@ -76,23 +80,38 @@ struct WordPoll {
   bool want[kChunk];
 };
 
-// Where this thread's word slots of one chunk land: hs offset k*NB + b and the
-// batch row b (offset -1: no word).  Computed once; integer division by a
-// runtime H costs tens of instructions, far too much to redo every step.
+// Where this thread's word slots of one chunk land: offset k*NB + b (f32
+// copy) or b*HS + k (f16 planes) of the copy, and the batch row b (offset
+// -1: no word).  Computed once; integer division by a runtime H costs tens of
+// instructions, far too much to redo every step.
 struct WordMap {
   int off[kChunk];
   int row[kChunk];
 };
 
-template <int NB>
-__device__ __forceinline__ void map_words(WordMap& m, int base, int H) {
+template <int NB, bool MF>
+__device__ __forceinline__ void map_words(WordMap& m, int base, int H, int HS) {
   const int n = NB * H;
 #pragma unroll
   for (int i = 0; i < kChunk; ++i) {
     const int e = base + i * kPollThreads;
     const int b = e / H;
-    m.off[i] = e < n ? (e - b * H) * NB + b : -1;
+    m.off[i] = e < n ? (MF ? b * HS + (e - b * H) : (e - b * H) * NB + b) : -1;
     m.row[i] = b;
+  }
+}
+
+// One value of h into the workgroup's copy: f32, or the hi/lo f16 pair (the
+// lo plane starts `lo` halves after the hi plane).
+template <bool MF>
+__device__ __forceinline__ void store_h(void* hs, int off, int lo, float v) {
+  if constexpr (MF) {
+    half_t* h16 = static_cast<half_t*>(hs);
+    const half_t hi = half_t(v);
+    h16[off] = hi;
+    h16[off + lo] = half_t(v - float(hi));
+  } else {
+    static_cast<float*>(hs)[off] = v;
   }
 }
 
@@ -106,8 +125,9 @@ __device__ __forceinline__ void poll_issue(WordPoll& w, const WordMap& m, const 
 }
 
 // Returns non-zero when the safety bound was hit.
+template <bool MF>
 __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, const unsigned long long* src, int base,
-                                             float* hs, unsigned tag) {
+                                             void* hs, int lo, unsigned tag) {
   int fail = 0;
   for (long round = 0;; ++round) {
     bool pending = false;
@@ -125,26 +145,34 @@ __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, cons
   }
 #pragma unroll
   for (int i = 0; i < kChunk; ++i)
-    if (w.want[i]) hs[m.off[i]] = __uint_as_float(static_cast<unsigned>(w.v[i]));
+    if (w.want[i]) store_h<MF>(hs, m.off[i], lo, __uint_as_float(static_cast<unsigned>(w.v[i])));
   return fail;
 }
 
 // Whole stage, run by the polling waves only (ptid = thread index among
 // them): the first chunk uses the precomputed map `m0`; further chunks (more
 // than kChunk words per polling thread) are mapped on the fly.
-template <int NB>
-__device__ __forceinline__ int stage_words(const unsigned long long* src, float* hs, unsigned tag, int H,
+template <int NB, bool MF>
+__device__ __forceinline__ int stage_words(const unsigned long long* src, void* hs, unsigned tag, int H, int HS,
                                            unsigned amask, const WordMap& m0, int ptid) {
   int fail = 0;
+  const int lo = NB * HS;
   WordPoll w;
   poll_issue(w, m0, src, ptid, amask);
-  fail |= poll_complete(w, m0, src, ptid, hs, tag);
+  fail |= poll_complete<MF>(w, m0, src, ptid, hs, lo, tag);
   for (int base = ptid + kPollThreads * kChunk; base < NB * H; base += kPollThreads * kChunk) {
     WordMap m;
-    map_words<NB>(m, base, H);
+    map_words<NB, MF>(m, base, H, HS);
     poll_issue(w, m, src, base, amask);
-    fail |= poll_complete(w, m, src, base, hs, tag);
+    fail |= poll_complete<MF>(w, m, src, base, hs, lo, tag);
   }
+  // Every load above has been consumed; this wait (free: nothing is
+  // outstanding) tells the compiler so.  Without it the word registers of
+  // words a thread did not want count as possibly still loading, and where
+  // the polling waves' path joins wave 0's the compiler then waits for all
+  // of wave 0's memory operations before reusing those registers, the
+  // exchange store included.
+  if constexpr (MF) __builtin_amdgcn_s_waitcnt(kWaitVm0);
   return fail;
 }
 
@@ -228,6 +256,74 @@ __device__ __forceinline__ void products(const T* Rl, int RS, const float* hs, f
   }
 }
 
+// Matrix-core variant of the products, for f16 R with the default
+// activations (h then stays within f16 range) and four or more batch rows.
+// R rows are the A operand, h the B operand as its hi and lo halves, each on
+// v_mfma_f32_16x16x32_f16 with f32 accumulation.  Wave w takes the 32-wide k
+// chunks w, w+4, ... of every 16-row block and writes its partial sums to
+// red[w][r][b]; the gate code adds the four partials in wave order.
+// Operand layout of the 16x16x32 product: lane l supplies row (A) or column
+// (B) l%16 with the 8 consecutive k from 8*(l/16); element i of the
+// accumulator of lane l is row 4*(l/16) + i, column l%16.  Columns at or past
+// NB repeat real columns and are dropped; rows past r_hi are clamped to the
+// last resident row and dropped.
+typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NB, int NRB>
+__device__ __forceinline__ void mfma_blocks(const half_t* Rl, int RS, const half_t* hhi, int HS, float* red, int r_lo,
+                                            int r_hi, int NR, int H4) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  f32x4 acc[NRB], accl[NRB];
+  const half_t* arow[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    acc[rb] = accl[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    arow[rb] = Rl + min(r_lo + 16 * rb + r16, NR - 1) * RS + 8 * q;
+  }
+  const half_t* bh = hhi + (r16 & (NB - 1)) * HS + 8 * q;
+  const half_t* bl = bh + NB * HS;
+  for (int kc = 32 * wave; kc < H4; kc += 128) {
+    const hx8 vh = *reinterpret_cast<const hx8*>(bh + kc);
+    const hx8 vl = *reinterpret_cast<const hx8*>(bl + kc);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const hx8 av = *reinterpret_cast<const hx8*>(arow[rb] + kc);
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, vh, acc[rb], 0, 0, 0);
+      accl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, vl, accl[rb], 0, 0, 0);
+    }
+  }
+  if (r16 < NB) {
+    float* out = red + wave * NR * NB + r16;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r_lo + 16 * rb + 4 * q + i;
+        if (r < r_hi) out[r * NB] = acc[rb][i] + accl[rb][i];
+      }
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void products_mfma(const half_t* Rl, int RS, const half_t* hhi, int HS, float* red,
+                                              int r_lo, int r_hi, int NR, int H4) {
+  switch ((r_hi - r_lo + 15) >> 4) {  // 16-row blocks: at most 4, since NB >= 4 allows 16 units, 64 rows
+    case 1: mfma_blocks<NB, 1>(Rl, RS, hhi, HS, red, r_lo, r_hi, NR, H4); break;
+    case 2: mfma_blocks<NB, 2>(Rl, RS, hhi, HS, red, r_lo, r_hi, NR, H4); break;
+    case 3: mfma_blocks<NB, 3>(Rl, RS, hhi, HS, red, r_lo, r_hi, NR, H4); break;
+    default: mfma_blocks<NB, 4>(Rl, RS, hhi, HS, red, r_lo, r_hi, NR, H4); break;
+  }
+}
+
+// Which products a kernel instance uses (host and device agree on it).
+template <typename T, int NB, bool DEF>
+constexpr bool mfma_products() {
+  return sizeof(T) == 2 && DEF && NB >= 4;
+}
+
 template <typename T, int NB, bool DEF>
 __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -242,11 +338,22 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   const int GH = G * H;
   const int H4 = (H + 31) & ~31;     // rows and h padded with zeros to a multiple of 32
   const int RS = H4 + 8;             // LDS row stride: the rows a wave reads start in different banks
+  constexpr bool MF = mfma_products<T, NB, DEF>();
+  const int HS = H4 + 8;             // row stride of the f16 planes of h
 
+  // LDS: R rows | copy of h | recurrent sums (f32 [NR][NB], or the four
+  // partials [4][NR][NB] of the matrix-core products)
   T* Rl = reinterpret_cast<T*>(smem);
   const size_t r_bytes = (size_t(p.NR) * RS * sizeof(T) + 15) & ~size_t(15);
-  float* hs = reinterpret_cast<float*>(smem + r_bytes);
-  float* rec = hs + NB * H4;
+  void* hs = smem + r_bytes;
+  float* rec = reinterpret_cast<float*>(smem + r_bytes + (MF ? size_t(4) * NB * HS : size_t(4) * NB * H4));
+  const int NRNB = p.NR * NB;
+  // recurrent sum of row r, batch row b
+  auto recv = [&](int r, int b) {
+    const int i = r * NB + b;
+    if constexpr (MF) return ((rec[i] + rec[NRNB + i]) + rec[2 * NRNB + i]) + rec[3 * NRNB + i];
+    else return rec[i];
+  };
 
   // R rows of this workgroup's units, resident for the whole layer
   const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * GH * H;
@@ -255,7 +362,13 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     const int gi = r / p.U, uu = r - gi * p.U;
     Rl[r * RS + k] = (uu < Uw && k < H) ? Rd[int64_t(p.gate_of[gi] * H + u0 + uu) * H + k] : T(0.f);
   }
-  for (int e = NB * H + tid; e < NB * H4; e += kPThreads) hs[e] = 0.f;  // padded tail of h stays zero
+  // padded tail of h stays zero (the f16 planes are cleared whole: columns of
+  // absent batch rows feed only dropped outputs, but must not hold Inf or NaN)
+  if constexpr (MF) {
+    for (int e = tid; e < 2 * NB * HS; e += kPThreads) static_cast<half_t*>(hs)[e] = half_t(0.f);
+  } else {
+    for (int e = NB * H + tid; e < NB * H4; e += kPThreads) static_cast<float*>(hs)[e] = 0.f;
+  }
 
   int maxL = 0;
   unsigned lens_left[NB];
@@ -311,10 +424,26 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
 
   int abort_run = 0;
   const int nrows_main = p.cand >= 0 ? p.cand * p.U : p.NR;  // rows of the first product
-  // this thread's slice of the projection, fetched one step ahead (HBM latency
-  // is about a step long, so the loads for step s+1 are issued during step s)
+  // this thread's slice of the projection for one step.  Vector-ALU
+  // products: prefetched one step ahead by wave 0 while the other waves poll
+  // (HBM latency is about a step long).  Matrix-core products: loaded at the
+  // end of the step before, after the exchange store, and first read by the
+  // next gate arithmetic, after the next stage wait: by then every memory
+  // operation of the wave issued before it has completed, so the wait for
+  // these registers costs nothing.  There the loads are unconditional (a
+  // lane with no element of its own, a gate block that does not exist or a
+  // step past the row's length loads an element that exists and ignores
+  // it): a load under a lane condition makes the compiler copy the
+  // registers and wait for every memory operation issued after it, the
+  // exchange stores included, whose completion takes a long trip.
   auto fetch_xw = [&](int step, float* out) {
-    if (gthread && step < L) {
+    if constexpr (MF) {
+      const int st = max(0, min(step, L - 1));
+      const int tt = rev ? max(0, L - 1 - st) : st;
+      const float* xw = a.xw + ((int64_t(d) * S + tt) * B + min(g_b, B - 1)) * GH + min(j, H - 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) out[g] = xw[min(g, G - 1) * H];
+    } else if (gthread && step < L) {
       const int tt = rev ? L - 1 - step : step;
       const float* xw = a.xw + ((int64_t(d) * S + tt) * B + g_b) * GH + j;
 #pragma unroll
@@ -325,15 +454,22 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   const bool poller = tid >= kPThreads - kPollThreads;
   const int ptid = tid - (kPThreads - kPollThreads);
   WordMap wmap;
-  if (poller) map_words<NB>(wmap, ptid, H);
-  float xnext[4] = {0.f, 0.f, 0.f, 0.f};
-  fetch_xw(0, xnext);
+  if (poller) map_words<NB, MF>(wmap, ptid, H, HS);
+  float xv[4] = {0.f, 0.f, 0.f, 0.f}, xnext[4] = {0.f, 0.f, 0.f, 0.f};
+  fetch_xw(0, MF ? xv : xnext);
   // output of the previous step, stored after the next step's word loads are issued
   float y_prev = 0.f;
   int64_t yi_prev = -1;
   auto store_y = [&]() {
     if (yi_prev >= 0) static_cast<T*>(p.Y)[yi_prev] = to_elem<T>(y_prev);
     yi_prev = -1;
+  };
+  auto run_products = [&](int r_lo, int r_hi) {
+    if constexpr (MF)
+      products_mfma<NB>(reinterpret_cast<const half_t*>(Rl), RS, static_cast<const half_t*>(hs), HS, rec, r_lo, r_hi,
+                        p.NR, H4);
+    else
+      products<T, NB>(Rl, RS, static_cast<const float*>(hs), rec, r_lo, r_hi, H4);
   };
   for (int s = 0; s < maxL; ++s) {
     unsigned amask = 0;
@@ -342,31 +478,32 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
 
     const bool live = gthread && s < L;
     const int t = rev ? L - 1 - s : s;
-    float xv[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) xv[g] = xnext[g];
 
     // 1. h of step s, every unit of this direction, active rows only (polling
-    // waves); meanwhile wave 0 stores the previous output and prefetches.
+    // waves); meanwhile wave 0 stores the previous output.
     int fail = 0;
     if (poller) {
-      fail = stage_words<NB>(a.xch + (s & 1) * DBH + dBH, hs, unsigned(s), H, amask, wmap, ptid);
+      fail = stage_words<NB, MF>(a.xch + (s & 1) * DBH + dBH, hs, unsigned(s), H, HS, amask, wmap, ptid);
     } else {
       store_y();
-      fetch_xw(s + 1, xnext);
+      if constexpr (!MF) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) xv[g] = xnext[g];
+        fetch_xw(s + 1, xnext);
+      }
     }
     if (fail) abort_flag = 1;
     lds_barrier();
     if ((abort_run = abort_flag) != 0) break;
 
     // 2. recurrent products of this workgroup's rows
-    products<T, NB>(Rl, RS, hs, rec, 0, nrows_main, H4);
+    run_products(0, nrows_main);
     lds_barrier();
 
     // 3. gate arithmetic
     float hnew = 0.f, z = 0.f;
     if (live) {
-      auto pre = [&](int gi, int g) { return pre_sum(xv[g], rec[(gi * p.U + g_uu) * NB + g_b], wb[g], rb[g]); };
+      auto pre = [&](int gi, int g) { return pre_sum(xv[g], recv(gi * p.U + g_uu, g_b), wb[g], rb[g]); };
       if (a.cell == RNN_CELL_LSTM) {
         float p4[4];
         p4[0] = pre(0, 0);
@@ -384,7 +521,7 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
         const float r = gru_gate<DEF>(pre(1, 1), a.clip, acts);
         if (p.cand < 0) {
           // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
-          const float ph = (xv[2] + r * (rec[(2 * p.U + g_uu) * NB + g_b] + rb[2])) + wb[2];
+          const float ph = (xv[2] + r * (recv(2 * p.U + g_uu, g_b) + rb[2])) + wb[2];
           hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
         } else {
           put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), r * hown);
@@ -396,15 +533,16 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
 
     if (p.cand >= 0) {
       // GRU, linear_before_reset = 0: the candidate needs r*h of every unit
-      if (poller && stage_words<NB>(a.xch2 + (s & 1) * DBH + dBH, hs, unsigned(s), H, amask, wmap, ptid))
+      if (poller &&
+          stage_words<NB, MF>(a.xch2 + (s & 1) * DBH + dBH, hs, unsigned(s), H, HS, amask, wmap, ptid))
         abort_flag = 1;
       lds_barrier();
       if ((abort_run = abort_flag) != 0) break;
-      products<T, NB>(Rl, RS, hs, rec, p.cand * p.U, p.NR, H4);
+      run_products(p.cand * p.U, p.NR);
       lds_barrier();
       if (live) {
         // h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
-        const float ph = pre_sum(xv[2], rec[(p.cand * p.U + g_uu) * NB + g_b], wb[2], rb[2]);
+        const float ph = pre_sum(xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2]);
         hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
       }
     }
@@ -422,6 +560,8 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
         if (p.Y_c) static_cast<T*>(p.Y_c)[sidx] = to_elem<T>(c);
       }
     }
+    // 4. the projection of step s+1, after the exchange store has gone out
+    if (MF && !poller) fetch_xw(s + 1, xv);
   }
   if (!abort_run && p.Y) store_y();
   if (abort_run && tid == 0) atomicExch(p.status, 1);
@@ -431,9 +571,12 @@ namespace {
 
 int next_pow2_nb(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 
-size_t lds_bytes(int NR, int H, int esize, int NB) {
+// LDS of one workgroup; `mf`: matrix-core products (f16 planes of h, four
+// partial sums per output).
+size_t lds_bytes(int NR, int H, int esize, int NB, bool mf) {
   const int H4 = (H + 31) & ~31;
   const size_t r = (size_t(NR) * (H4 + 8) * esize + 15) & ~size_t(15);
+  if (mf) return r + size_t(4) * NB * (H4 + 8) + size_t(4) * NR * NB * 4;
   return r + size_t(NB) * H4 * 4 + size_t(NR) * NB * 4;
 }
 
@@ -470,7 +613,8 @@ bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per
     wpd = int((p.H + U - 1) / U);
   }
   if (U * NB > 64) return false;  // one gate thread per (unit, batch row), all in wave 0
-  if (lds_bytes(Gp * U, int(p.H), p.esize, NB) > kLdsLimit) return false;
+  const bool mf = p.esize == 2 && NB >= 4 && default_acts(p);
+  if (lds_bytes(Gp * U, int(p.H), p.esize, NB, mf) > kLdsLimit) return false;
   *blocks = wpd * p.D;
   *units = U;
   *wg_per_dir = wpd;
@@ -531,9 +675,9 @@ hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const Per
   pa.Y_c = io.Y_c;
   pa.status = io.status;
   const int NB = next_pow2_nb(a.B);
-  const size_t lds = lds_bytes(pa.NR, a.H, p.esize, NB);
   const int blocks = p.pers_blocks;
   const bool def = default_acts(p);
+  const size_t lds = lds_bytes(pa.NR, a.H, p.esize, NB, p.esize == 2 && NB >= 4 && def);
 #define RNN_PERS_CASE(T, NB)                                                      \
   return def ? launch_nb<T, NB, true>(pa, blocks, lds, s) : launch_nb<T, NB, false>(pa, blocks, lds, s)
   if (a.dtype == RNN_DTYPE_F32) {

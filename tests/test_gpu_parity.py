@@ -113,6 +113,34 @@ def test_matrix_options(cell, direction, layout, dtype, engine):
         check(spec, make_inputs(spec, 18), engine=engine, what=f"LSTM input_forget {direction} L{layout} {dtype}")
 
 
+# f16 layers with the default activations and four to eight batch rows take
+# the persistent engine's matrix-core products: one to four 16-row blocks per
+# workgroup, k chunks that do not split evenly over the four waves (or leave
+# waves without a chunk), partial last workgroups, both GRU forms.
+PERS_MFMA_CASES = [
+    # cell, direction, layout, option, B, H
+    ("LSTM", "bidirectional", 0, "peep", 4, 100),     # 64 rows: four blocks
+    ("LSTM", "forward", 1, "input_forget", 3, 300),   # 48 rows: three blocks
+    ("LSTM", "reverse", 1, "peep", 8, 256),           # 32 rows: two blocks
+    ("GRU", "bidirectional", 0, "lbr0", 8, 520),      # 16 + 8 rows, two products
+    ("GRU", "forward", 1, "lbr1", 5, 33),             # 24 rows, k chunks on two waves only
+    ("GRU", "reverse", 0, "lbr0", 4, 70),             # 32 + 16 rows
+    ("RNN", "bidirectional", 0, "", 6, 1000),         # 8 rows, 32 k chunks
+    ("RNN", "forward", 1, "", 4, 17),                 # 16 rows, one k chunk
+]
+
+
+@pytest.mark.parametrize("cell,direction,layout,opt,B,H", PERS_MFMA_CASES,
+                         ids=[f"{c[0]}-{c[1]}-L{c[2]}-{c[3]}-B{c[4]}-H{c[5]}" for c in PERS_MFMA_CASES])
+def test_persistent_matrix_products(cell, direction, layout, opt, B, H):
+    spec = LayerSpec(cell, seq=11, batch=B, input=45, hidden=H, direction=direction, layout=layout, dtype="f16",
+                     linear_before_reset=1 if opt == "lbr1" else 0, input_forget=1 if opt == "input_forget" else 0,
+                     peephole=opt == "peep", clip=3.0 if cell == "LSTM" else None, init_h=True,
+                     init_c=cell == "LSTM", lens=True, outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 31, Dists(sequence_lens=("I", 0, 11), W=("U", -0.2, 0.2), R=("U", -0.2, 0.2)))
+    check(spec, inp, engine="persistent", what=f"persistent mfma {cell}/{direction}/L{layout}/{opt}/B{B}/H{H}")
+
+
 LARGE = [(c, d, dt) for c in ("LSTM", "GRU", "RNN") for d in ("forward", "bidirectional") for dt in ("f32", "f16")]
 
 
