@@ -172,6 +172,25 @@ CONFIGS = {
         dists=Dists(W=("U", -0.02, 0.02), R=("U", -0.02, 0.02), B=("U", -0.05, 0.05)),
         seed=5,
         name="biRNN S1024 B256 I1024 H2048 f32 L0 Relu/ScaledTanh"),
+    # The text-line recognizer shapes the "Recurrent layers" page tests
+    # ("Tolerance and evidence"): bidirectional LSTMs of sequence 80 and 48,
+    # batch 1 and 8, input 256 and 192, hidden 256 and 96.  The page gives
+    # no distributions; these follow C2 (uniform weights of scale
+    # about 1/sqrt(hidden), N(0,1) inputs, N(0, 0.5) initial states).
+    "REC80": dict(
+        spec=LayerSpec("LSTM", seq=80, batch=1, input=256, hidden=256, direction="bidirectional",
+                       dtype="f32", init_h=True, init_c=True, outputs=("Y", "Y_h", "Y_c")),
+        dists=Dists(W=("U", -1 / 16, 1 / 16), R=("U", -1 / 16, 1 / 16), B=("U", -0.1, 0.1),
+                    initial_h=("N", 0.0, 0.5), initial_c=("N", 0.0, 0.5)),
+        seed=6,
+        name="biLSTM S80 B1 I256 H256 f32 L0 (recognizer)"),
+    "REC48": dict(
+        spec=LayerSpec("LSTM", seq=48, batch=8, input=192, hidden=96, direction="bidirectional",
+                       dtype="f32", init_h=True, init_c=True, outputs=("Y", "Y_h", "Y_c")),
+        dists=Dists(W=("U", -0.1, 0.1), R=("U", -0.1, 0.1), B=("U", -0.1, 0.1),
+                    initial_h=("N", 0.0, 0.5), initial_c=("N", 0.0, 0.5)),
+        seed=7,
+        name="biLSTM S48 B8 I192 H96 f32 L0 (recognizer)"),
 }
 
 

@@ -281,6 +281,21 @@ FULL = [("C1", {}), ("C2", {}), ("C3", {"linear_before_reset": 0}), ("C3", {"lin
 SAMPLE_ROWS = {"C4": [0, 9, 31, 63], "C5": [0, 255]}
 
 
+# The recognizer shapes of the "Recurrent layers" page: both layer shapes,
+# both tensor types, every engine, both layouts, with every operand and output
+# at an odd element offset and sentinels around every output (H = 96 does not
+# divide the persistent engine's 32-wide padding nor the 64-unit tiles).
+REC_CASES = [(n, dt, e, lay) for n in ("REC80", "REC48") for dt in ("f32", "f16")
+             for e in ("auto", "launch", "persistent") for lay in (0, 1)]
+
+
+@pytest.mark.parametrize("name,dtype,engine,layout", REC_CASES, ids=["-".join(map(str, c)) for c in REC_CASES])
+def test_recognizer_shapes(name, dtype, engine, layout):
+    spec, inp = synth.config(name, dtype=dtype, layout=layout)
+    offs = {n: 5 for n in list(inp) + list(spec.outputs)}
+    check(spec, inp, engine=engine, offsets=offs, what=f"recognizer {name} {dtype} L{layout}")
+
+
 def test_engine_choice_and_plan():
     import onnx_recurrent_layers_amd as rl
     for name in ("C1", "C2", "C3"):
