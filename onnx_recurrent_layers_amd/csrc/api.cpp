@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -160,6 +161,14 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   if (engine == RNN_ENGINE_PERSISTENT && !pers_ok)
     return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
   p->engine = engine;
+  // f32 projections of 2^32 flops and more run as three bf16 products (the
+  // f32 matrix cores have a sixteenth of the bf16 rate); RNN_F32_SPLIT=0 or 1
+  // overrides the choice, so that tests reach both forms on any shape.
+  if (desc->dtype == RNN_DTYPE_F32) {
+    const double flops = 2.0 * double(p->D) * double(p->S) * double(p->B) * double(GH) * double(p->I);
+    p->f32_split_proj = flops >= 4294967296.0;
+    if (const char* e = std::getenv("RNN_F32_SPLIT")) p->f32_split_proj = std::atoi(e) != 0;
+  }
 
   StateLayout& st = p->st;
   st = StateLayout{};
@@ -385,6 +394,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     pa.D = p.D;
     pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
     pa.H = p.H;
+    pa.f32_split = p.f32_split_proj;
     // the state setup rides in the same launch (extra workgroups)
     if ((e = launch_projection(pa, sa, p.desc.dtype, s)) != hipSuccess)
       return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));

@@ -47,6 +47,9 @@ struct Problem {
   int pers_blocks = 0;       // workgroups of the cooperative launch
   int pers_units = 0;        // units per workgroup
   int pers_wg_per_dir = 0;
+  // f32 tensors: the projection on the bf16 matrix cores (three split
+  // products) instead of the f32 matrix cores
+  bool f32_split_proj = false;
 };
 
 // Arguments shared by the step kernels.
@@ -83,6 +86,7 @@ struct ProjArgs {
   int D;
   int skip_block;     // gate block of H columns not needed (input_forget: f), or -1
   int64_t H;
+  int f32_split;      // f32 tensors: products on the bf16 matrix cores as three split products
 };
 
 struct SetupArgs {

@@ -56,6 +56,46 @@ def test_projection_scratch(dtype, layout):
         assert err <= 1e-4, (d, err)
 
 
+# f32 tensors with the projection on the bf16 matrix cores (three split
+# products, forced with RNN_F32_SPLIT=1 on small shapes).  Each element of Xw
+# must lie within 2^-15 * sum_k |x_k * w_k| of the exact product: the split
+# leaves residuals of at most 2^-16 of each |x_k * w_k|, and f32 accumulation
+# of K terms adds below K * 2^-24 of the same sum.
+@pytest.mark.parametrize("layout,S,B,I,H", [(0, 13, 11, 70, 37), (1, 9, 21, 130, 72), (0, 3, 40, 1024, 64)])
+def test_projection_scratch_bf16x3(layout, S, B, I, H, monkeypatch):
+    import torch
+    monkeypatch.setenv("RNN_F32_SPLIT", "1")
+    spec = LayerSpec("GRU", seq=S, batch=B, input=I, hidden=H, layout=layout, dtype="f32",
+                     direction="bidirectional", outputs=("Y_h",))
+    inp = make_inputs(spec, 8)
+    note(f"case projection bf16x3 L{layout} S{S} B{B} I{I} H{H}")
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    D, G = 2, 3
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
+    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
+    A = X.reshape(S * B, I)
+    for d in range(D):
+        ref = oracle.projection(A, inp["W"][d])
+        bound = 2.0 ** -15 * (np.abs(A.astype(np.float64)) @ np.abs(inp["W"][d].astype(np.float64)).T) + 1e-30
+        err = np.abs(xw[d].astype(np.float64) - ref)
+        assert np.all(err <= bound), (d, float(np.max(err / bound)))
+        assert np.max(err) <= 1e-4
+
+
+@pytest.mark.parametrize("cell", ["LSTM", "GRU", "RNN"])
+def test_layers_with_bf16x3_projection(cell, monkeypatch):
+    """Whole f32 layers with the split projection, on both engines."""
+    monkeypatch.setenv("RNN_F32_SPLIT", "1")
+    for engine, B in (("launch", 37), ("persistent", 5), ("launch", 3)):
+        spec = LayerSpec(cell, seq=9, batch=B, input=200, hidden=48, direction="bidirectional", dtype="f32",
+                         layout=B % 2, init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM",
+                         clip=2.5, linear_before_reset=1 if (B == 5 and cell == "GRU") else 0,
+                         outputs=("Y", "Y_h", "Y_c"))
+        inp = make_inputs(spec, 41, Dists(sequence_lens=("I", 0, 9)))
+        check(spec, inp, engine=engine, what=f"bf16x3 projection {cell} {engine} B{B}")
+
+
 @pytest.mark.parametrize("layout,cell,input_forget,S,B,I,H", [
     (0, "LSTM", 0, 13, 11, 72, 40),      # ragged M, N and K tails, several tiles
     (1, "LSTM", 1, 9, 70, 136, 256),     # skipped f block of whole tiles, layout 1
