@@ -4,7 +4,7 @@
 Default workload: bidirectional LSTM, seq 80, batch 1, input 256, hidden 256,
 f32, layout 0 (the five seeded workloads are in onnx_recurrent_layers_amd.synth;
 ``--config`` picks another).  A step of this benchmark is one whole layer
-(projection, state setup, every recurrent step, output pass) through
+(projection, state setup, every recurrent step, the outputs) through
 ``rnn_encode`` with inputs resident in device memory.
 
 Prints one JSON line: timesteps/s (value), layer latency (ms_per_step), the

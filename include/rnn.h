@@ -133,15 +133,17 @@ void rnn_problem_destroy(rnn_problem* problem);
  *   *xw_bytes    = 4 * D * S * B * G * H: the f32 input projection, laid out
  *                  time-major [D][S][B][G*H] (row t*B+b of direction d holds
  *                  X[t,b,:] . W[d]^T);
- *   *state_bytes = the f32 hidden state after every step, the cell state,
- *                  and the persistent engine's exchange words.
+ *   *state_bytes = the f32 hidden state (two slots of [D][B][H]), the f32
+ *                  cell state, the GRU two-pass buffers, or the persistent
+ *                  engine's exchange words.
  * Either may be 0 (then the matching pointer may be NULL).  Both buffers must
  * be 256-byte aligned; they may be two regions of one arena. */
 int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state_bytes);
 
 /* Enqueue one layer on `stream` (a hipStream_t; NULL is the default stream).
- * Stages: the input projection, the state setup, the recurrent steps, and one
- * output pass for whichever of Y, Y_h, Y_c is requested.  Batch = 0 enqueues
+ * Stages: the input projection (carrying the state setup), then the
+ * recurrent steps, which write whichever of Y, Y_h, Y_c is requested as they
+ * go (the setup writes the outputs no step reaches).  Batch = 0 enqueues
  * nothing; Seq = 0 writes only Y_h / Y_c (initial states or zeros).  All
  * checks run before the first launch; on error nothing is enqueued.
  * sequence_lens is read on the device and not validated there. */
@@ -150,8 +152,9 @@ int rnn_encode(const rnn_problem* problem, const rnn_operands* operands,
 
 /* rnn_encode with timing marks: the same launches, plus hipEventRecord of
  * events[i] (a hipEvent_t, or NULL to skip that mark) on `stream` at the
- * stage boundaries: [0] before the projection, [1] before the state setup,
- * [2] before the recurrent steps, [3] before the output pass, [4] after it.
+ * stage boundaries: [0] before the projection, [1] before the state setup
+ * (its own launch only when Seq = 0), [2] before the recurrent steps, [3]
+ * after them, [4] at the end (the outputs have no pass of their own).
  * Lets a caller time each stage with events on the stream the kernels run on. */
 int rnn_encode_timed(const rnn_problem* problem, const rnn_operands* operands,
                      void* xw_scratch, void* state_scratch, void* stream, void* const events[5]);

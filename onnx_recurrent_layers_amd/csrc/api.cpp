@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI: validation, planning, scratch sizing and the launch
 // sequence of one layer ("Recurrent layers" page, "How a layer runs": input
-// projection, state setup, the recurrent steps, the output passes).
+// projection, state setup, the recurrent steps, the outputs written by the
+// steps themselves).
 //
 // Every check runs in 64-bit checked arithmetic before anything is enqueued
 // (the page's "Scratch" paragraph); messages name the cell and the argument.
@@ -149,9 +150,6 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   p->xw_bytes = (p->S > 0 && p->B > 0) ? size_t(xw) : 0;
   int64_t dbh;
   if (!mul3(p->D, p->B, p->H, &dbh) || dbh > kMaxBytes / 8) return bad(RNN_ERR_SHAPE, "state: size overflows");
-  int64_t slab;
-  if (!mul_ok(p->steps + 1, dbh, &slab) || !mul_ok(slab, 4, &slab) || slab > kMaxBytes)
-    return bad(RNN_ERR_SHAPE, "state scratch: size overflows");
   // Engine choice.
   int blocks = 0, units = 0, wpd = 0;
   const bool pers_ok = persistent_supported(*p, &blocks, &units, &wpd);
@@ -181,7 +179,7 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     st.xch2 = off;  off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
     st.status = off; off = align256(off + 4);
   } else {
-    st.slab = off;  off = align256(off + size_t(slab));
+    st.hbuf = off;  off = align256(off + 2 * size_t(dbh) * 4);
     st.cell = off;  off = align256(off + size_t(dbh) * 4);
     st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
     st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
@@ -237,9 +235,9 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
   info->step_blocks = p->engine == RNN_ENGINE_PERSISTENT ? p->pers_blocks : 0;
   int n = 0;
   if (p->B > 0) {
-    n += 1;                        // projection with the state setup (or the setup alone when Seq = 0)
+    n += 1;                        // projection with the state setup (or the setup alone when Seq = 0); the
+                                   // steps and the setup write the outputs
     if (p->S > 0) n += step_launch_count(*p);
-    if (p->engine != RNN_ENGINE_PERSISTENT) n += 1;  // output pass (the persistent engine writes outputs itself)
   }
   info->launches = n;
   info->step_launches = (p->B > 0 && p->S > 0) ? step_launch_count(*p) : 0;
@@ -324,7 +322,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* st = static_cast<char*>(state_scratch);
   const bool pers = p.engine == RNN_ENGINE_PERSISTENT;
-  float* slab = pers ? nullptr : reinterpret_cast<float*>(st + p.st.slab);
+  float* hbuf = pers ? nullptr : reinterpret_cast<float*>(st + p.st.hbuf);
   float* cstate = pers ? nullptr : reinterpret_cast<float*>(st + p.st.cell);
   int* status = pers ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
 
@@ -337,12 +335,20 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.dtype = p.desc.dtype;
   sa.init_h = ih;
   sa.init_c = ic;
-  sa.slab = slab;
+  sa.hbuf = hbuf;
   sa.cell_state = cstate;
   sa.xch = pers ? reinterpret_cast<unsigned long long*>(st + p.st.xch) : nullptr;
   sa.xch2 = (pers && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
                 ? reinterpret_cast<unsigned long long*>(st + p.st.xch2) : nullptr;
   sa.status = status;
+  if (!pers) {
+    sa.Y = const_cast<char*>(Y);
+    sa.Y_h = const_cast<char*>(Yh);
+    sa.Y_c = const_cast<char*>(Yc);
+    sa.lens = reinterpret_cast<const int32_t*>(lens);
+    sa.S = int(p.S);
+    sa.steps = int(p.steps);
+  }
 
   StepArgs a{};
   a.cell = cell;
@@ -360,7 +366,11 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   a.P = P;
   a.lens = reinterpret_cast<const int32_t*>(lens);
   a.xw = static_cast<const float*>(xw_scratch);
-  a.slab = slab;
+  a.hbuf = hbuf;
+  a.Y = const_cast<char*>(Y);
+  a.Y_h = const_cast<char*>(Yh);
+  a.Y_c = const_cast<char*>(Yc);
+  a.layout = p.desc.layout;
   a.cell_state = cstate;
   a.zbuf = reinterpret_cast<float*>(st + p.st.zbuf);
   a.rhbuf = reinterpret_cast<float*>(st + p.st.rhbuf);
@@ -419,26 +429,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     }
   }
   if ((e = mark(3)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
-  // 4. outputs (the persistent engine writes them itself)
-  if (!pers && (Y || Yh || Yc)) {
-    OutputArgs oa{};
-    oa.D = p.D;
-    oa.B = int(p.B);
-    oa.H = int(p.H);
-    oa.S = int(p.S);
-    oa.steps = int(p.steps);
-    oa.layout = p.desc.layout;
-    oa.dtype = p.desc.dtype;
-    oa.dir_reverse[0] = a.dir_reverse[0];
-    oa.dir_reverse[1] = a.dir_reverse[1];
-    oa.lens = a.lens;
-    oa.slab = slab;
-    oa.cell_state = cstate;
-    oa.Y = const_cast<char*>(Y);
-    oa.Y_h = const_cast<char*>(Yh);
-    oa.Y_c = const_cast<char*>(Yc);
-    if ((e = launch_output(oa, s)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "output launch: %s", hipGetErrorString(e));
-  }
+  // 4. outputs: written by the steps and the state setup (no pass of their own)
   if ((e = mark(4)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
   return RNN_OK;
 }

@@ -16,6 +16,20 @@
 
 namespace rnnhip {
 
+// Outputs of one (direction d, batch row b, unit j) after a step at time t:
+// Y, and after the row's last step (`last`) the final states Y_h and Y_c,
+// rounded to the tensor type.  Null outputs are skipped.
+template <typename T>
+__device__ __forceinline__ void store_outputs(const StepArgs& a, int d, int b, int j, int t, bool last, float h,
+                                              float c) {
+  if (a.Y) static_cast<T*>(a.Y)[y_index(a.layout, a.S, a.D, a.B, a.H, t, d, b, j)] = to_elem<T>(h);
+  if (last) {
+    const int64_t si = state_index(a.layout, a.D, a.B, a.H, d, b, j);
+    if (a.Y_h) static_cast<T*>(a.Y_h)[si] = to_elem<T>(h);
+    if (a.Y_c) static_cast<T*>(a.Y_c)[si] = to_elem<T>(c);
+  }
+}
+
 template <bool DEF>
 __device__ __forceinline__ float act_sig(const Act& a, float x) {
   if constexpr (DEF) return sigmoid_f(x);

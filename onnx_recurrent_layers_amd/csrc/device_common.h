@@ -82,11 +82,26 @@ __device__ __forceinline__ int row_length(const int32_t* lens, int b, int S, int
   return L < steps ? L : steps;
 }
 
+// Index of output Y at time t, direction d, batch row b, unit j:
+// layout 0 [S][D][B][H], layout 1 [B][S][D][H].
+__device__ __forceinline__ int64_t y_index(int layout, int S, int D, int B, int H, int t, int d, int b, int j) {
+  return layout == 0 ? ((int64_t(t) * D + d) * B + b) * H + j : ((int64_t(b) * S + t) * D + d) * H + j;
+}
+
+// Index of a state tensor (initial_h, initial_c, Y_h, Y_c) for direction d,
+// batch row b, unit j: layout 0 [D][B][H], layout 1 [B][D][H].
+__device__ __forceinline__ int64_t state_index(int layout, int D, int B, int H, int d, int b, int j) {
+  return layout == 0 ? (int64_t(d) * B + b) * H + j : (int64_t(b) * D + d) * H + j;
+}
+
 // Stage 2 ("Recurrent layers" page, "How a layer runs", item 2): the first
 // hidden and cell state from initial_h / initial_c or zeros, for one share of
 // the (d, b, j) elements (`part` of `parts` workgroups): slot 0 of the
 // per-step state, the cell state, and for the persistent engine the tagged
-// exchange words of step 0 with the other slots marked empty.
+// exchange words of step 0 with the other slots marked empty.  For the
+// per-step engine it also writes the outputs that no step writes ("Semantics"
+// rules): Y is zero past each row's length, a row of length 0 has zero final
+// states, and Seq = 0 gives the initial states as final states.
 template <typename T>
 __device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int parts) {
   const int64_t DBH = int64_t(a.D) * a.B * a.H;
@@ -98,7 +113,7 @@ __device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int pa
     const int64_t src = a.layout == 0 ? i : (b * a.D + d) * a.H + j;
     const float h0 = a.init_h ? ld(static_cast<const T*>(a.init_h), src) : 0.f;
     const float c0 = a.init_c ? ld(static_cast<const T*>(a.init_c), src) : 0.f;
-    if (a.slab) a.slab[i] = h0;
+    if (a.hbuf) a.hbuf[i] = h0;
     if (a.cell_state) a.cell_state[i] = c0;
     if (a.xch) {
       // word = (tag << 32) | value bits; slot 0 carries step 0, slot 1 no step yet.
@@ -108,6 +123,16 @@ __device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int pa
     if (a.xch2) {
       a.xch2[i] = 0xffffffffull << 32;
       a.xch2[DBH + i] = 0xffffffffull << 32;
+    }
+    if (a.Y || a.Y_h || a.Y_c) {
+      const int L = a.S > 0 ? row_length(a.lens, int(b), a.S, a.steps) : 0;
+      if (a.Y)
+        for (int t = L; t < a.S; ++t)
+          static_cast<T*>(a.Y)[y_index(a.layout, a.S, a.D, a.B, a.H, t, int(d), int(b), int(j))] = to_elem<T>(0.f);
+      if (L == 0) {
+        if (a.Y_h) static_cast<T*>(a.Y_h)[src] = to_elem<T>(a.S == 0 ? h0 : 0.f);
+        if (a.Y_c) static_cast<T*>(a.Y_c)[src] = to_elem<T>(a.S == 0 ? c0 : 0.f);
+      }
     }
   }
   if (a.status && part == 0 && threadIdx.x == 0) *a.status = 0;

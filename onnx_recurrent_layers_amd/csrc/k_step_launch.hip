@@ -9,7 +9,9 @@
 // k = lane, lane+64, ... in increasing order and the 64 partial sums are
 // combined by a fixed xor butterfly: the summation order depends only on the
 // shapes, never on scheduling (no atomics), so runs are bit-identical.
-// Rows whose sequence has ended are skipped: nothing reads their later slots.
+// Rows whose sequence has ended are skipped: their h stays in the state slot
+// of their last step, and nothing reads it again.  Each step writes Y (and,
+// after a row's last step, Y_h / Y_c) itself.
 #include "cells.h"
 
 namespace rnnhip {
@@ -44,8 +46,8 @@ __global__ __launch_bounds__(64) void step_launch_kernel(StepArgs a, int s, int 
 
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
-  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
-  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
+  const float* hprev = a.hbuf + int64_t(s & 1) * DBH + dBH;
+  float* hnext = a.hbuf + int64_t((s + 1) & 1) * DBH + dBH;
   const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * G * H * H;
   const bool gru_two_phase = a.cell == RNN_CELL_GRU && !a.lbr;
 
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(64) void step_launch_kernel(StepArgs a, int s, int 
     lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
     *cst = c;
     hnext[sidx] = h;
+    store_outputs<T>(a, d, b, j, t, s == Lr - 1, h, c);
   } else if (a.cell == RNN_CELL_GRU) {
     if (!gru_two_phase) {
       // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
@@ -140,7 +143,9 @@ __global__ __launch_bounds__(64) void step_launch_kernel(StepArgs a, int s, int 
       const float wb = bias ? ld(bias, n) : 0.f;
       const float rb = bias ? ld(bias, GH + n) : 0.f;
       const float ph = (xw[n] + r * (rec[2] + rb)) + wb;
-      hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+      const float h = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+      hnext[sidx] = h;
+      store_outputs<T>(a, d, b, j, t, s == Lr - 1, h, 0.f);
     } else if (phase == 0) {
       const float z = gru_gate(pre(0), a.clip, acts);
       const float r = gru_gate(pre(1), a.clip, acts);
@@ -149,10 +154,14 @@ __global__ __launch_bounds__(64) void step_launch_kernel(StepArgs a, int s, int 
     } else {
       // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
       const float z = a.zbuf[dBH + sidx];
-      hnext[sidx] = gru_unit(z, pre(2), hprev[sidx], a.clip, acts);
+      const float h = gru_unit(z, pre(2), hprev[sidx], a.clip, acts);
+      hnext[sidx] = h;
+      store_outputs<T>(a, d, b, j, t, s == Lr - 1, h, 0.f);
     }
   } else {
-    hnext[sidx] = rnn_unit(pre(0), a.clip, acts);
+    const float h = rnn_unit(pre(0), a.clip, acts);
+    hnext[sidx] = h;
+    store_outputs<T>(a, d, b, j, t, s == Lr - 1, h, 0.f);
   }
 }
 

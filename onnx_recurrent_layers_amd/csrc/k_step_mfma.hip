@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_kernel(MfmaStepArgs m) {
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
   const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
-  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
   const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * G * H * H;
 
   // Staging: segment q of a chunk is row q / (kBK/kSeg), elements
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kMThreads) void step_mfma_h16_kernel(MfmaStepArgs m
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
   const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
-  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
   const half_t* Rd = static_cast<const half_t*>(a.R) + int64_t(d) * G * H * H;
 
   // A: segments of 4 f32 (16 bytes); B: segments of 8 halves (16 bytes)

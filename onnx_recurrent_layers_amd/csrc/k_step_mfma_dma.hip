@@ -97,6 +97,7 @@ struct EpiIn {
   float cprev;     // LSTM cell state
   float hprev;     // GRU previous hidden state
   float z;         // GRU linear_before_reset = 0, second pass: z of the first
+  int len;         // the row's length
   bool live;       // the element exists and its row still runs at this step
 };
 
@@ -110,11 +111,15 @@ struct EpiCtx {
   const float* xw;      // this direction's Xw, [S][B][G*H]
   const float* hprev;   // h of this step, [B][H]
   float* hnext;         // h of the next step, [B][H]
+  void* Y;              // outputs (or null), written as the step finishes each element
+  void* Y_h;
+  void* Y_c;
   float* cst;           // LSTM cell state, [B][H]
   float* zbuf;          // GRU z of the first pass, [B][H]
   float* rhbuf;         // GRU r*h, [B][H]
   float clip;
   int H, B, GH, s, cell, lbr, phase, input_forget, has_p, rev, Gp;
+  int S, D, d, layout;
   int gate[4];
   Act act[3];
 };
@@ -151,8 +156,15 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
   }
   const int64_t DBH = int64_t(a.D) * a.B * a.H, dBH = int64_t(d) * a.B * a.H;
   c.xw = a.xw + int64_t(d) * a.S * a.B * c.GH;
-  c.hprev = a.slab + int64_t(m.step) * DBH + dBH;
-  c.hnext = a.slab + int64_t(m.step + 1) * DBH + dBH;
+  c.hprev = a.hbuf + int64_t(m.step & 1) * DBH + dBH;
+  c.hnext = a.hbuf + int64_t((m.step + 1) & 1) * DBH + dBH;
+  c.Y = a.Y;
+  c.Y_h = a.Y_h;
+  c.Y_c = a.Y_c;
+  c.S = a.S;
+  c.D = a.D;
+  c.d = d;
+  c.layout = a.layout;
   c.cst = a.cell_state + dBH;
   c.zbuf = a.zbuf + dBH;
   c.rhbuf = a.rhbuf + dBH;
@@ -187,6 +199,7 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
   const int r = e >> ujs, u = e & ((1 << ujs) - 1);
   const int b = b0 + r, j = j0 + u;
   const int L = e < n_el ? len_s[r] : 0;
+  o.len = L;
   o.live = b < c.B && j < H && s < L;
   if (j >= H) return;
   // the unit's biases and peepholes, also for a row that does not run: the
@@ -216,6 +229,18 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
   } else if (c.cell == RNN_CELL_GRU) {
     o.hprev = c.hprev[si];
     if (!c.lbr && c.phase == 1) o.z = c.zbuf[si];
+  }
+}
+
+// Y of one finished element and, after its row's last step, Y_h / Y_c.
+template <typename RT>
+__device__ __forceinline__ void epi_outputs(const EpiCtx& c, int b, int j, int L, float h, float cc) {
+  const int t = c.rev ? (L - 1 - c.s) : c.s;
+  if (c.Y) static_cast<RT*>(c.Y)[y_index(c.layout, c.S, c.D, c.B, c.H, t, c.d, b, j)] = to_elem<RT>(h);
+  if (c.s == L - 1) {
+    const int64_t si = state_index(c.layout, c.D, c.B, c.H, c.d, b, j);
+    if (c.Y_h) static_cast<RT*>(c.Y_h)[si] = to_elem<RT>(h);
+    if (c.Y_c) static_cast<RT*>(c.Y_c)[si] = to_elem<RT>(cc);
   }
 }
 
@@ -255,13 +280,16 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
       lstm_unit<DEF>(p4, nullptr, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
     c.cst[si] = cc;
     c.hnext[si] = h;
+    epi_outputs<RT>(c, b, j, o.len, h, cc);
   } else if (c.cell == RNN_CELL_GRU) {
     if (c.lbr) {
       // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
       const float z = gru_gate<DEF>(pre(0), c.clip, acts);
       const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
       const float ph = (o.xv[2] + rg * (rrow[2 * UJ] + widen<RT>(o.rb[2], odd))) + widen<RT>(o.wb[2], odd);
-      c.hnext[si] = gru_unit<DEF>(z, ph, o.hprev, c.clip, acts);
+      const float h = gru_unit<DEF>(z, ph, o.hprev, c.clip, acts);
+      c.hnext[si] = h;
+      epi_outputs<RT>(c, b, j, o.len, h, 0.f);
     } else if (c.phase == 0) {
       const float z = gru_gate<DEF>(pre(0), c.clip, acts);
       const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
@@ -269,10 +297,14 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
       c.rhbuf[si] = rg * o.hprev;
     } else {
       // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
-      c.hnext[si] = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
+      const float h = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
+      c.hnext[si] = h;
+      epi_outputs<RT>(c, b, j, o.len, h, 0.f);
     }
   } else {
-    c.hnext[si] = rnn_unit<DEF>(pre(0), c.clip, acts);
+    const float h = rnn_unit<DEF>(pre(0), c.clip, acts);
+    c.hnext[si] = h;
+    epi_outputs<RT>(c, b, j, o.len, h, 0.f);
   }
 }
 
@@ -329,7 +361,8 @@ __device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& fi
     const int e = tid + k * kMThreads;
     const int r = e >> ujs, b = b0 + r;
     EpiIn o = first;
-    o.live = b < c.B && j < c.H && c.s < len_s[r];
+    o.len = len_s[r];
+    o.live = b < c.B && j < c.H && c.s < o.len;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi)
       if (gi < c.Gp) o.xv[gi] = planes[gi * n_el + e];
@@ -372,7 +405,7 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
   const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
-  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.slab + int64_t(s) * DBH + dBH;
+  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
   const RT* Rd = static_cast<const RT*>(a.R) + int64_t(d) * G * H * H;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u), kRsrcWord3);

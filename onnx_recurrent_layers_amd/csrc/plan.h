@@ -21,7 +21,7 @@ struct Act {
 
 // Byte offsets of the regions inside the caller's state scratch.
 struct StateLayout {
-  size_t slab;     // f32 h after every step: [steps+1][D][B][H]; slot 0 = initial h
+  size_t hbuf;     // f32 h, two slots of [D][B][H]: slot s & 1 holds h of step s (slot 0 = initial h)
   size_t cell;     // f32 c: [D][B][H] (LSTM), updated in place, final after the last step
   size_t zbuf;     // f32 GRU z for the two-phase step: [D][B][H]
   size_t rhbuf;    // f32 GRU r*h for the two-phase step: [D][B][H]
@@ -63,7 +63,11 @@ struct StepArgs {
   const void* P;           // [D][3*H] or null
   const int32_t* lens;     // [B] or null
   const float* xw;         // [D][S][B][G*H]
-  float* slab;             // [steps+1][D][B][H]
+  float* hbuf;             // [2][D][B][H]: slot s & 1 holds h of step s
+  void* Y;                 // [S][D][B][H] (layout 0) or [B][S][D][H] (layout 1), or null
+  void* Y_h;               // [D][B][H] (layout 0) or [B][D][H] (layout 1), or null
+  void* Y_c;               // the same (LSTM), or null
+  int layout;
   float* cell_state;       // [D][B][H]
   float* zbuf;             // [D][B][H]
   float* rhbuf;            // [D][B][H]
@@ -95,11 +99,19 @@ struct SetupArgs {
   int dtype;
   const void* init_h;  // or null
   const void* init_c;  // or null
-  float* slab;         // slot 0, or null (persistent engine)
+  float* hbuf;         // slot 0 of the per-step engine's h, or null (persistent engine)
   float* cell_state;   // or null (persistent engine)
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
   int* status;               // persistent engine status word, or null
+  // outputs no step of the per-step engine writes (null for the persistent
+  // engine, which writes them itself): Y past each row's length, the final
+  // states of rows of length 0, and every final state when Seq = 0
+  void* Y;
+  void* Y_h;
+  void* Y_c;
+  const int32_t* lens;
+  int S, steps;
 };
 
 // What the persistent engine reads and writes besides StepArgs.
@@ -112,23 +124,8 @@ struct PersistentIO {
   int* status;
 };
 
-struct OutputArgs {
-  int D, B, H, S;
-  int steps;
-  int layout;
-  int dtype;
-  int dir_reverse[2];
-  const int32_t* lens;
-  const float* slab;
-  const float* cell_state;
-  void* Y;     // or null
-  void* Y_h;   // or null
-  void* Y_c;   // or null
-};
-
 hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s);  // also runs the state setup
 hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
-hipError_t launch_output(const OutputArgs& a, hipStream_t s);
 hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);

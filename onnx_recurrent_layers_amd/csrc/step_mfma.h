@@ -47,8 +47,8 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
   const int GH = G * H;
   const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
   const Act* acts = a.act + d * a.slots;
-  const float* hprev = a.slab + int64_t(s) * DBH + dBH;
-  float* hnext = a.slab + int64_t(s + 1) * DBH + dBH;
+  const float* hprev = a.hbuf + int64_t(s & 1) * DBH + dBH;
+  float* hnext = a.hbuf + int64_t((s + 1) & 1) * DBH + dBH;
   for (int e = tid; e < BM * UJ; e += kMThreads) {
     const int r = e / UJ, u = e - r * UJ;
     const int b = b0 + r, j = j0 + u;
@@ -90,6 +90,7 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
       lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
       *cst = c;
       hnext[sidx] = h;
+      store_outputs<T>(a, d, b, j, t, s == L - 1, h, c);
     } else if (a.cell == RNN_CELL_GRU) {
       if (a.lbr) {
         // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
@@ -99,7 +100,9 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
         const float wb = bias ? ld(bias, n) : 0.f;
         const float rbv = bias ? ld(bias, GH + n) : 0.f;
         const float ph = (xw[n] + rg * (rrow[2 * UJ + u] + rbv)) + wb;
-        hnext[sidx] = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+        const float h = gru_unit(z, ph, hprev[sidx], a.clip, acts);
+        hnext[sidx] = h;
+        store_outputs<T>(a, d, b, j, t, s == L - 1, h, 0.f);
       } else if (m.phase == 0) {
         const float z = gru_gate(pre(0, 0), a.clip, acts);
         const float rg = gru_gate(pre(1, 1), a.clip, acts);
@@ -111,10 +114,14 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
         const float wb = bias ? ld(bias, n) : 0.f;
         const float rbv = bias ? ld(bias, GH + n) : 0.f;
         const float ph = pre_sum(xw[n], rrow[u], wb, rbv);
-        hnext[sidx] = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
+        const float h = gru_unit(a.zbuf[dBH + sidx], ph, hprev[sidx], a.clip, acts);
+        hnext[sidx] = h;
+        store_outputs<T>(a, d, b, j, t, s == L - 1, h, 0.f);
       }
     } else {
-      hnext[sidx] = rnn_unit(pre(0, 0), a.clip, acts);
+      const float h = rnn_unit(pre(0, 0), a.clip, acts);
+      hnext[sidx] = h;
+      store_outputs<T>(a, d, b, j, t, s == L - 1, h, 0.f);
     }
   }
 }

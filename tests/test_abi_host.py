@@ -97,7 +97,7 @@ def test_scratch_sizes(lib, cell, direction, G):
     xw, st = rl.rnn_scratch_size(h)
     D = 2 if direction == "bidirectional" else 1
     assert xw == 4 * D * 7 * 3 * G * 5
-    assert st >= 4 * (7 + 1) * D * 3 * 5
+    assert st >= 4 * 2 * D * 3 * 5   # two slots of f32 h
     assert st % 256 == 0
     rl.rnn_problem_destroy(h)
 
@@ -110,7 +110,7 @@ def test_empty_batch_and_seq_sizes(lib):
     h = rl.rnn_problem_create(rl.make_desc(spec("LSTM", seq=0)))
     xw, st = rl.rnn_scratch_size(h)
     assert xw == 0 and st > 0
-    assert rl.rnn_problem_plan(h).launches == 2   # setup + outputs (no projection when Seq = 0)
+    assert rl.rnn_problem_plan(h).launches == 1   # the setup, which also writes the final states (no projection)
     rl.rnn_problem_destroy(h)
 
 
@@ -120,7 +120,7 @@ def test_launch_plan_one_pass_per_step(lib, cell, lbr, per_step):
     h = rl.rnn_problem_create(rl.make_desc(s, "launch"))
     info = rl.rnn_problem_plan(h)
     assert info.engine == rl.ENGINES["launch"] and info.steps == 6
-    assert info.launches == 1 + 6 * per_step + 1   # projection carrying the state setup, steps, outputs
+    assert info.launches == 1 + 6 * per_step   # projection carrying the state setup, then the steps (which write the outputs)
     assert info.step_launches == 6 * per_step
     rl.rnn_problem_destroy(h)
 
