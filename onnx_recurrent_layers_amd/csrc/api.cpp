@@ -167,6 +167,19 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     p->f32_split_proj = flops >= 4294967296.0;
     if (const char* e = std::getenv("RNN_F32_SPLIT")) p->f32_split_proj = std::atoi(e) != 0;
   }
+  // Likewise the per-step matrix-core product of f32 layers from 2^28 flops
+  // per step on (h and R as bf16 hi/lo planes; R is split once per layer).
+  if (desc->dtype == RNN_DTYPE_F32 && engine == RNN_ENGINE_LAUNCH && mfma_step_supported(*p)) {
+    StepArgs t{};
+    t.G = p->G;
+    t.D = p->D;
+    t.H = int(p->H);
+    t.B = int(p->B);
+    const double flops = 2.0 * double(p->D) * double(p->B) * double(GH) * double(p->H);
+    bool want = flops >= 268435456.0;
+    if (const char* e = std::getenv("RNN_F32_SPLIT")) want = std::atoi(e) != 0;
+    p->f32_split_step = want && step_dma_supported(t, 2);
+  }
 
   StateLayout& st = p->st;
   st = StateLayout{};
@@ -183,6 +196,11 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     st.cell = off;  off = align256(off + size_t(dbh) * 4);
     st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
     st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+    if (p->f32_split_step) {
+      st.rsplit = off;  off = align256(off + 2 * size_t(p->D) * size_t(GH) * size_t(p->H) * 2);
+      st.hsplit = off;  off = align256(off + 4 * size_t(dbh) * 2);
+      st.rhsplit = off; off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 2 : 0));
+    }
   }
   st.total = p->B > 0 ? off : 0;
 
@@ -336,6 +354,9 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.init_h = ih;
   sa.init_c = ic;
   sa.hbuf = hbuf;
+  unsigned short* rsplit = p.f32_split_step ? reinterpret_cast<unsigned short*>(st + p.st.rsplit) : nullptr;
+  unsigned short* hsplit = p.f32_split_step ? reinterpret_cast<unsigned short*>(st + p.st.hsplit) : nullptr;
+  sa.hsplit = hsplit;
   sa.cell_state = cstate;
   sa.xch = pers ? reinterpret_cast<unsigned long long*>(st + p.st.xch) : nullptr;
   sa.xch2 = (pers && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
@@ -367,6 +388,10 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   a.lens = reinterpret_cast<const int32_t*>(lens);
   a.xw = static_cast<const float*>(xw_scratch);
   a.hbuf = hbuf;
+  a.rsplit = rsplit;
+  a.hsplit = hsplit;
+  a.rhsplit = (p.f32_split_step && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
+                  ? reinterpret_cast<unsigned short*>(st + p.st.rhsplit) : nullptr;
   a.Y = const_cast<char*>(Y);
   a.Y_h = const_cast<char*>(Yh);
   a.Y_c = const_cast<char*>(Yc);
@@ -423,6 +448,8 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     } else {
       // batches of 16 and more: the product of each step on the matrix cores
       const bool mfma = mfma_step_supported(p);
+      if (p.f32_split_step && (e = launch_split_r(R, rsplit, int64_t(p.D) * p.G * p.H * p.H, s)) != hipSuccess)
+        return fail(RNN_ERR_HIP, cell, "R split launch: %s", hipGetErrorString(e));
       for (int step = 0; step < int(p.steps); ++step)
         if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
           return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));

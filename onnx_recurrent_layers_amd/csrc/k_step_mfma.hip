@@ -495,8 +495,9 @@ hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipSt
     m.UJ = uj;
     hipError_t e;
     const bool h16 = a.dtype == RNN_DTYPE_F16 && p.def_acts;
-    if ((h16 || a.dtype == RNN_DTYPE_F32) && step_dma_supported(a, h16)) {
-      e = launch_step_dma(m, bm, h16, s);
+    const int mode = p.f32_split_step ? 2 : h16 ? 1 : 0;
+    if (mode == 2 || ((h16 || a.dtype == RNN_DTYPE_F32) && step_dma_supported(a, mode))) {
+      e = launch_step_dma(m, bm, mode, s);
     } else if (h16) {
       e = bm == 64 ? launch_h16<64>(m, a.H, a.B, a.D, s)
                    : bm == 32 ? launch_h16<32>(m, a.H, a.B, a.D, s) : launch_h16<16>(m, a.H, a.B, a.D, s);

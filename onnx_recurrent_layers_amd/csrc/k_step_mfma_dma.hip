@@ -7,11 +7,16 @@
 // Tile and arithmetic are those of the other matrix-core step: a workgroup
 // owns BM batch rows x UJ units of one direction with all Gp gate blocks of
 // those units (product tile [BM] x [Gp*UJ], K = H), and finishes the gate
-// arithmetic itself.  Two modes:
+// arithmetic itself.  Three modes:
 //   mode 0, f32 tensors: v_mfma_f32_16x16x4_f32 on f32 h and f32 R;
 //   mode 1, f16 tensors with the default activations: h split into
 //     hi = f16(h) and lo = f16(h - hi), R.hi + R.lo on v_mfma_f32_16x16x32_f16
-//     with separate f32 accumulators (f16 products are exact in f32).
+//     with separate f32 accumulators (f16 products are exact in f32);
+//   mode 2, large f32 layers: h and R as bf16 hi/lo planes (R split once per
+//     layer, h by the step that produces it), each product taken as
+//     lo_h.hi_R + hi_h.lo_R + hi_h.hi_R on v_mfma_f32_16x16x32_bf16 with one
+//     f32 accumulator: bf16 x bf16 products are exact in f32, and what the
+//     split drops is below 2^-16 of each |h.R|.
 // The k order is fixed (chunks in increasing order, a fixed order within a
 // chunk), so runs are bit-identical.
 //
@@ -33,6 +38,7 @@
 namespace rnnhip {
 
 typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
 
 
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond every resource size used here
@@ -65,6 +71,12 @@ template <> struct DmaGeo<1> {           // f32 h split on the fly, f16 R
   typedef half_t RT;
   static constexpr int KC = 128;
   static constexpr int ASEGS = 32;
+  static constexpr int BELEMS = 8;
+};
+template <> struct DmaGeo<2> {           // bf16 hi/lo planes of h and R (f32 tensors)
+  typedef float RT;
+  static constexpr int KC = 64;          // a row of a chunk: 8 hi segments, then 8 lo segments
+  static constexpr int ASEGS = 16;
   static constexpr int BELEMS = 8;
 };
 
@@ -117,6 +129,9 @@ struct EpiCtx {
   float* cst;           // LSTM cell state, [B][H]
   float* zbuf;          // GRU z of the first pass, [B][H]
   float* rhbuf;         // GRU r*h, [B][H]
+  unsigned short* hsn;  // mode 2: h of the next step as bf16 hi/lo planes (lo at +DBH), or null
+  unsigned short* rhs;  // mode 2: GRU r*h as bf16 hi/lo planes, or null
+  int64_t DBH;
   float clip;
   int H, B, GH, s, cell, lbr, phase, input_forget, has_p, rev, Gp;
   int S, D, d, layout;
@@ -166,6 +181,9 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
   c.d = d;
   c.layout = a.layout;
   c.cst = a.cell_state + dBH;
+  c.DBH = DBH;
+  c.hsn = a.hsplit ? a.hsplit + int64_t((m.step + 1) & 1) * 2 * DBH + dBH : nullptr;
+  c.rhs = a.rhsplit ? a.rhsplit + dBH : nullptr;
   c.zbuf = a.zbuf + dBH;
   c.rhbuf = a.rhbuf + dBH;
   const RT* bias = a.bias ? static_cast<const RT*>(a.bias) + int64_t(d) * 2 * c.GH : nullptr;
@@ -232,6 +250,12 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
   }
 }
 
+// h of the next step: f32, and in mode 2 also its bf16 planes.
+__device__ __forceinline__ void epi_put_h(const EpiCtx& c, int64_t si, float h) {
+  c.hnext[si] = h;
+  if (c.hsn) split_bf16_bits(h, c.hsn[si], c.hsn[c.DBH + si]);
+}
+
 // Y of one finished element and, after its row's last step, Y_h / Y_c.
 template <typename RT>
 __device__ __forceinline__ void epi_outputs(const EpiCtx& c, int b, int j, int L, float h, float cc) {
@@ -279,7 +303,7 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
     else
       lstm_unit<DEF>(p4, nullptr, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
     c.cst[si] = cc;
-    c.hnext[si] = h;
+    epi_put_h(c, si, h);
     epi_outputs<RT>(c, b, j, o.len, h, cc);
   } else if (c.cell == RNN_CELL_GRU) {
     if (c.lbr) {
@@ -288,22 +312,24 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
       const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
       const float ph = (o.xv[2] + rg * (rrow[2 * UJ] + widen<RT>(o.rb[2], odd))) + widen<RT>(o.wb[2], odd);
       const float h = gru_unit<DEF>(z, ph, o.hprev, c.clip, acts);
-      c.hnext[si] = h;
+      epi_put_h(c, si, h);
       epi_outputs<RT>(c, b, j, o.len, h, 0.f);
     } else if (c.phase == 0) {
       const float z = gru_gate<DEF>(pre(0), c.clip, acts);
       const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
       c.zbuf[si] = z;
-      c.rhbuf[si] = rg * o.hprev;
+      const float rh = rg * o.hprev;
+      c.rhbuf[si] = rh;
+      if (c.rhs) split_bf16_bits(rh, c.rhs[si], c.rhs[c.DBH + si]);
     } else {
       // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
       const float h = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
-      c.hnext[si] = h;
+      epi_put_h(c, si, h);
       epi_outputs<RT>(c, b, j, o.len, h, 0.f);
     }
   } else {
     const float h = rnn_unit<DEF>(pre(0), c.clip, acts);
-    c.hnext[si] = h;
+    epi_put_h(c, si, h);
     epi_outputs<RT>(c, b, j, o.len, h, 0.f);
   }
 }
@@ -405,12 +431,31 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
   const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
-  const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
-  const RT* Rd = static_cast<const RT*>(a.R) + int64_t(d) * G * H * H;
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<RT*>(Rd), 0, int(unsigned(G) * unsigned(H) * unsigned(H) * unsigned(sizeof(RT))), kRsrcWord3);
+  // operand resources.  Mode 2 reads bf16 planes: the hi plane of this
+  // direction, with the lo plane `plane_a` (`plane_b`) bytes further on, and
+  // the resource reaching to the end of this direction's lo plane.
+  __amdgpu_buffer_rsrc_t ra, rb;
+  unsigned plane_a = 0, plane_b = 0;
+  if constexpr (MODE == 2) {
+    const unsigned short* hs2 = cand_phase ? a.rhsplit + dBH : a.hsplit + int64_t(s & 1) * 2 * DBH + dBH;
+    const unsigned short* rs2 = a.rsplit + int64_t(d) * G * H * H;
+    plane_a = unsigned(DBH) * 2u;
+    plane_b = unsigned(a.D) * unsigned(G) * unsigned(H) * unsigned(H) * 2u;
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(hs2), 0,
+                                           int(plane_a + unsigned(B) * unsigned(H) * 2u), kRsrcWord3);
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(rs2), 0,
+                                           int(plane_b + unsigned(G) * unsigned(H) * unsigned(H) * 2u), kRsrcWord3);
+  } else {
+    const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
+    const RT* Rd = static_cast<const RT*>(a.R) + int64_t(d) * G * H * H;
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u),
+                                           kRsrcWord3);
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(Rd), 0,
+                                           int(unsigned(G) * unsigned(H) * unsigned(H) * unsigned(sizeof(RT))),
+                                           kRsrcWord3);
+  }
+  constexpr unsigned AES = MODE == 2 ? 2u : 4u;              // bytes of an element of h as loaded
+  constexpr unsigned BES = MODE == 2 ? 2u : unsigned(sizeof(RT));  // ... of R
 
   // h segments of this lane: load i of the wave fills LDS bytes
   // [(wave*LA + i) * 1024, +1024) of the chunk, lane l the 16 bytes at 16*l
@@ -421,7 +466,7 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
     const int p = (wave * LA + i) * 64 + lane;
     const int r = p / ASEGS;
     aseg[i] = (p % ASEGS) ^ (r & 15);
-    arow[i] = b0 + r < B ? unsigned(b0 + r) * unsigned(H) * 4u : kOutOfRange;
+    arow[i] = b0 + r < B ? unsigned(b0 + r) * unsigned(H) * AES : kOutOfRange;
   }
   // R segments: wave w owns column blocks w and w + 4 (CB of them); load i of
   // a block fills its rows 4i..4i+3
@@ -435,16 +480,22 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
       const int c = ci * 16 + 4 * i + (lane >> 4);
       const int gi = c >> ujs, u = c & (UJ - 1);
       const bool ok = ci < ncb && j0 + u < H;
-      brow[cb][i] = ok ? unsigned(gate_block(m, gi) * H + j0 + u) * unsigned(H) * unsigned(sizeof(RT)) : kOutOfRange;
+      brow[cb][i] = ok ? unsigned(gate_block(m, gi) * H + j0 + u) * unsigned(H) * BES : kOutOfRange;
     }
   auto slot = [&](int i) -> unsigned char* { return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3; };
   auto fetch = [&](int kc, unsigned char* st) {
     const int k0 = kc * KC;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int k = k0 + aseg[i] * 4;
       // a row outside the tile starts at the out-of-range marker, so row + k stays out of range
-      const unsigned off = k < H ? arow[i] + unsigned(k) * 4u : kOutOfRange;
+      unsigned off;
+      if constexpr (MODE == 2) {   // logical segment: plane (hi, lo) and 8-element k group
+        const int k = k0 + (aseg[i] & 7) * 8;
+        off = k < H ? arow[i] + (aseg[i] >> 3) * plane_a + unsigned(k) * 2u : kOutOfRange;
+      } else {
+        const int k = k0 + aseg[i] * 4;
+        off = k < H ? arow[i] + unsigned(k) * 4u : kOutOfRange;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, RNN_LDS_PTR(st + (wave * LA + i) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
@@ -452,8 +503,15 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 4 * i + (lane >> 4);
-        const int k = k0 + (bseg0 ^ rr) * BELEMS;
-        const unsigned off = k < H ? brow[cb][i] + unsigned(k) * unsigned(sizeof(RT)) : kOutOfRange;
+        unsigned off;
+        if constexpr (MODE == 2) {
+          const int ls = bseg0 ^ rr;
+          const int k = k0 + (ls & 7) * 8;
+          off = k < H ? brow[cb][i] + (ls >> 3) * plane_b + unsigned(k) * 2u : kOutOfRange;
+        } else {
+          const int k = k0 + (bseg0 ^ rr) * BELEMS;
+          off = k < H ? brow[cb][i] + unsigned(k) * BES : kOutOfRange;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, RNN_LDS_PTR(st + C::A_BYTES + ((wave + 4 * cb) * 16 + 4 * i) * 256), 16, off, 0, 0, 0);
       }
@@ -535,6 +593,37 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
 #pragma unroll
             for (int bi = 0; bi < NBI; ++bi)
               acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[bi][j][e], bq[cb][j][e], acc[cb][bi], 0, 0, 0);
+    } else if constexpr (MODE == 2) {
+      // step kk takes the 8-element k groups 4kk + q of both planes, the same
+      // groups for h and R
+      bx8 bh[CB][2], bl[CB][2];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const unsigned char* row = Bs + ((wave + 4 * cb) * 16 + r16) * 256;
+          bh[cb][kk] = *reinterpret_cast<const bx8*>(row + (((4 * kk + q) ^ r16) << 4));
+          bl[cb][kk] = *reinterpret_cast<const bx8*>(row + (((8 + 4 * kk + q) ^ r16) << 4));
+        }
+      bx8 ah[NBI][2], al[NBI][2];
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const unsigned char* row = st + (bi * 16 + r16) * 256;
+          ah[bi][kk] = *reinterpret_cast<const bx8*>(row + (((4 * kk + q) ^ r16) << 4));
+          al[bi][kk] = *reinterpret_cast<const bx8*>(row + (((8 + 4 * kk + q) ^ r16) << 4));
+        }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int bi = 0; bi < NBI; ++bi) {
+            acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[bi][kk], bh[cb][kk], acc[cb][bi], 0, 0, 0);
+            acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bi][kk], bl[cb][kk], acc[cb][bi], 0, 0, 0);
+            acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bi][kk], bh[cb][kk], acc[cb][bi], 0, 0, 0);
+          }
     } else {
       hx8 bv[CB][4];
 #pragma unroll
@@ -627,7 +716,18 @@ static hipError_t launch_bm(const MfmaStepArgs& m, hipStream_t s) {
   return launch_cfg<MODE, BM, 2>(m, s);
 }
 
-bool step_dma_supported(const StepArgs& a, bool h16) {
+bool step_dma_supported(const StepArgs& a, int mode) {
+  if (mode == 2) {
+    // bf16 planes in the state scratch (16-byte aligned rows when H is a
+    // multiple of 8); every offset plus a plane, and the out-of-range marker
+    // above them, fits 31 bits
+    if (a.H % 8 != 0) return false;
+    const uint64_t r = uint64_t(a.G) * a.H * a.H;
+    if ((uint64_t(a.D) + 1) * r * 2 >= kOutOfRange) return false;
+    if ((uint64_t(a.D) + 1) * a.B * a.H * 2 >= kOutOfRange) return false;
+    return true;
+  }
+  const bool h16 = mode == 1;
   const int seg = h16 ? 8 : 4;   // elements of a 16-byte segment of R
   const uint64_t esize = h16 ? 2 : 4;
   if (a.H % seg != 0 || reinterpret_cast<uintptr_t>(a.R) % 16 != 0) return false;
@@ -637,9 +737,11 @@ bool step_dma_supported(const StepArgs& a, bool h16) {
   return true;
 }
 
-hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, bool h16, hipStream_t s) {
-  if (h16)
+hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, int mode, hipStream_t s) {
+  if (mode == 1)
     return bm == 64 ? launch_bm<1, 64>(m, s) : bm == 32 ? launch_bm<1, 32>(m, s) : launch_bm<1, 16>(m, s);
+  if (mode == 2)
+    return bm == 64 ? launch_bm<2, 64>(m, s) : bm == 32 ? launch_bm<2, 32>(m, s) : launch_bm<2, 16>(m, s);
   return bm == 64 ? launch_bm<0, 64>(m, s) : bm == 32 ? launch_bm<0, 32>(m, s) : launch_bm<0, 16>(m, s);
 }
 

@@ -25,6 +25,9 @@ struct StateLayout {
   size_t cell;     // f32 c: [D][B][H] (LSTM), updated in place, final after the last step
   size_t zbuf;     // f32 GRU z for the two-phase step: [D][B][H]
   size_t rhbuf;    // f32 GRU r*h for the two-phase step: [D][B][H]
+  size_t rsplit;   // bf16 R as two planes (hi, lo) of [D][G*H][H] (f32 layers on the bf16 matrix cores)
+  size_t hsplit;   // bf16 h, two slots of two planes (hi, lo) of [D][B][H]
+  size_t rhsplit;  // bf16 GRU r*h, two planes of [D][B][H]
   size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
   size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
   size_t status;   // int: persistent engine status (1: a wait hit its safety bound)
@@ -50,6 +53,8 @@ struct Problem {
   // f32 tensors: the projection on the bf16 matrix cores (three split
   // products) instead of the f32 matrix cores
   bool f32_split_proj = false;
+  // f32 tensors: the per-step matrix-core product on the bf16 matrix cores
+  bool f32_split_step = false;
 };
 
 // Arguments shared by the step kernels.
@@ -71,6 +76,11 @@ struct StepArgs {
   float* cell_state;       // [D][B][H]
   float* zbuf;             // [D][B][H]
   float* rhbuf;            // [D][B][H]
+  // f32 layers whose step product runs on the bf16 matrix cores (null
+  // otherwise): bf16 bit patterns, hi and lo planes of each tensor
+  unsigned short* rsplit;  // [2][D][G*H][H]
+  unsigned short* hsplit;  // [2 slots][2][D][B][H]: slot s & 1 holds h of step s
+  unsigned short* rhsplit; // [2][D][B][H]
   unsigned long long* xch; // [2][D][B][H]
   unsigned long long* xch2;// [2][D][B][H]
   float clip;              // > 0: clamp
@@ -100,6 +110,7 @@ struct SetupArgs {
   const void* init_h;  // or null
   const void* init_c;  // or null
   float* hbuf;         // slot 0 of the per-step engine's h, or null (persistent engine)
+  unsigned short* hsplit;  // slot 0 of h as bf16 hi and lo planes, or null
   float* cell_state;   // or null (persistent engine)
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
@@ -126,10 +137,15 @@ struct PersistentIO {
 
 hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s);  // also runs the state setup
 hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
+hipError_t launch_split_r(const void* R, unsigned short* rsplit, int64_t n, hipStream_t s);
 hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);
 bool mfma_step_supported(const Problem& p);
+// Whether the direct-to-LDS matrix-core step takes this shape in a mode (0:
+// f32 on the f32 matrix cores, 1: f16 with split h, 2: f32 on the bf16 matrix
+// cores).
+bool step_dma_supported(const StepArgs& a, int mode);
 hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const PersistentIO& io, hipStream_t s);
 bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per_dir);
 

@@ -128,9 +128,9 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
 
 // The matrix-core step whose operands go straight from global memory into
 // LDS (k_step_mfma_dma.hip): usable when R rows and h rows are whole 16-byte
-// segments and every byte offset fits 32 bits.  h16 selects the split-h f16
-// mode (f16 tensors, default activations); otherwise f32 tensors.
-bool step_dma_supported(const StepArgs& a, bool h16);
-hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, bool h16, hipStream_t s);
+// segments and every byte offset fits 32 bits.  mode 0: f32 tensors on the
+// f32 matrix cores; 1: f16 tensors with the default activations (split h);
+// 2: f32 tensors on the bf16 matrix cores (h and R as bf16 hi/lo planes).
+hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, int mode, hipStream_t s);
 
 }  // namespace rnnhip

@@ -232,6 +232,36 @@ def test_matrix_step_direct_to_lds(cell, dtype, direction, layout, opt, B, H, ti
     check(spec, inp, engine="launch", what=f"lds-direct {cell}/{dtype}/{direction}/L{layout}/opt{opt}/B{B}/H{H}/{tile}")
 
 
+# f32 layers whose per-step product runs on the bf16 matrix cores (h and R as
+# bf16 hi/lo planes, three split products), forced with RNN_F32_SPLIT=1 on
+# small layers: every cell, both GRU forms, every tile shape, ragged batch
+# and a partial last k chunk, non-default activations.
+SPLIT_CASES = [
+    # cell, direction, layout, option, B, H, tile, activations
+    ("LSTM", "bidirectional", 0, 0, 37, 64, "16x16", None),
+    ("LSTM", "forward", 1, 1, 40, 136, "32x32", None),
+    ("GRU", "bidirectional", 0, 0, 70, 136, "64x32", None),
+    ("GRU", "reverse", 1, 1, 20, 256, "32x16", None),
+    ("RNN", "bidirectional", 0, 0, 33, 520, "64x64", (("Relu", 0, 0), ("ScaledTanh", 1.5, 0.5))),
+    ("RNN", "forward", 1, 0, 64, 128, None, (("Softsign", 0, 0),)),
+    ("GRU", "forward", 0, 0, 17, 96, "64x16", (("HardSigmoid", 0.2, 0.5), ("Elu", 0.9, 0))),
+]
+
+
+@pytest.mark.parametrize("cell,direction,layout,opt,B,H,tile,acts", SPLIT_CASES,
+                         ids=["-".join(map(str, c[:7])) for c in SPLIT_CASES])
+def test_matrix_step_bf16x3(cell, direction, layout, opt, B, H, tile, acts, monkeypatch):
+    monkeypatch.setenv("RNN_F32_SPLIT", "1")
+    if tile:
+        monkeypatch.setenv("RNN_MFMA_TILE", tile)
+    spec = LayerSpec(cell, seq=7, batch=B, input=40, hidden=H, direction=direction, layout=layout, dtype="f32",
+                     linear_before_reset=opt if cell == "GRU" else 0, input_forget=opt if cell == "LSTM" else 0,
+                     init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM", clip=2.0,
+                     acts=acts, outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 43, Dists(sequence_lens=("I", 0, 7), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    check(spec, inp, engine="launch", what=f"bf16x3 step {cell}/{direction}/L{layout}/opt{opt}/B{B}/H{H}/{tile}")
+
+
 def test_large_batch_general_activations():
     """The matrix-core step kernel with non-default activations (f16 tensors
     then take the f32 path, f32 tensors always do)."""
