@@ -155,21 +155,11 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   const bool pers_ok = persistent_supported(*p, &blocks, &units, &wpd);
   int engine = desc->engine;
   if (p->S == 0 || p->steps == 0 || p->B == 0) engine = RNN_ENGINE_LAUNCH;  // nothing to step
-  if (engine == RNN_ENGINE_AUTO) engine = pers_ok ? RNN_ENGINE_PERSISTENT : RNN_ENGINE_LAUNCH;
-  if (engine == RNN_ENGINE_PERSISTENT && !pers_ok)
-    return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
-  p->engine = engine;
-  // f32 projections of 2^32 flops and more run as three bf16 products (the
-  // f32 matrix cores have a sixteenth of the bf16 rate); RNN_F32_SPLIT=0 or 1
-  // overrides the choice, so that tests reach both forms on any shape.
-  if (desc->dtype == RNN_DTYPE_F32) {
-    const double flops = 2.0 * double(p->D) * double(p->S) * double(p->B) * double(GH) * double(p->I);
-    p->f32_split_proj = flops >= 4294967296.0;
-    if (const char* e = std::getenv("RNN_F32_SPLIT")) p->f32_split_proj = std::atoi(e) != 0;
-  }
-  // Likewise the per-step matrix-core product of f32 layers from 2^28 flops
-  // per step on (h and R as bf16 hi/lo planes; R is split once per layer).
-  if (desc->dtype == RNN_DTYPE_F32 && engine == RNN_ENGINE_LAUNCH && mfma_step_supported(*p)) {
+  // f32 layers whose per-step matrix-core product is 2^28 flops or more run it
+  // on the bf16 matrix cores (h and R as bf16 hi/lo planes; R is split once
+  // per layer); RNN_F32_SPLIT=0 or 1 overrides the choice, as for the
+  // projection below.
+  if (desc->dtype == RNN_DTYPE_F32 && !pers_ok && mfma_step_supported(*p)) {
     StepArgs t{};
     t.G = p->G;
     t.D = p->D;
@@ -180,11 +170,37 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     if (const char* e = std::getenv("RNN_F32_SPLIT")) want = std::atoi(e) != 0;
     p->f32_split_step = want && step_dma_supported(t, 2);
   }
+  // Batches of 16 and more: the matrix-core step, in one cooperative launch
+  // when its tiles fit the chip (else one launch per step).  The automatic
+  // choice takes the cooperative launch only for f16 layers with the default
+  // activations (split h): there it measured faster than one launch per step
+  // (LSTM 256/64/1024/1024: 2.41 against 2.53 ms of steps), while for f32
+  // layers it measured slower (RNN 1024/256/1024/2048 in bf16 split mode:
+  // 35 against 33 ms).
+  int mfma_tiles = 0;
+  const bool pers_mfma_ok =
+      !pers_ok && p->S > 0 && p->steps > 0 && p->B > 0 && mfma_persistent_supported(*p, &mfma_tiles);
+  const bool pers_mfma_auto = pers_mfma_ok && desc->dtype == RNN_DTYPE_F16 && p->def_acts;
+  if (engine == RNN_ENGINE_AUTO)
+    engine = (pers_ok || pers_mfma_auto) ? RNN_ENGINE_PERSISTENT : RNN_ENGINE_LAUNCH;
+  if (engine == RNN_ENGINE_PERSISTENT && !pers_ok && !pers_mfma_ok)
+    return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
+  p->engine = engine;
+  p->pers_mfma = engine == RNN_ENGINE_PERSISTENT && !pers_ok;
+  if (p->pers_mfma) p->pers_blocks = mfma_tiles;
+  // f32 projections of 2^32 flops and more run as three bf16 products (the
+  // f32 matrix cores have a sixteenth of the bf16 rate); RNN_F32_SPLIT=0 or 1
+  // overrides the choice, so that tests reach both forms on any shape.
+  if (desc->dtype == RNN_DTYPE_F32) {
+    const double flops = 2.0 * double(p->D) * double(p->S) * double(p->B) * double(GH) * double(p->I);
+    p->f32_split_proj = flops >= 4294967296.0;
+    if (const char* e = std::getenv("RNN_F32_SPLIT")) p->f32_split_proj = std::atoi(e) != 0;
+  }
 
   StateLayout& st = p->st;
   st = StateLayout{};
   size_t off = 0;
-  if (engine == RNN_ENGINE_PERSISTENT) {
+  if (engine == RNN_ENGINE_PERSISTENT && !p->pers_mfma) {
     p->pers_blocks = blocks;
     p->pers_units = units;
     p->pers_wg_per_dir = wpd;
@@ -200,6 +216,10 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
       st.rsplit = off;  off = align256(off + 2 * size_t(p->D) * size_t(GH) * size_t(p->H) * 2);
       st.hsplit = off;  off = align256(off + 4 * size_t(dbh) * 2);
       st.rhsplit = off; off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 2 : 0));
+    }
+    if (p->pers_mfma) {
+      st.flags = off;   off = align256(off + size_t(kPersistentMfmaTiles) * 4);
+      st.status = off;  off = align256(off + 4);
     }
   }
   st.total = p->B > 0 ? off : 0;
@@ -256,6 +276,7 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
     n += 1;                        // projection with the state setup (or the setup alone when Seq = 0); the
                                    // steps and the setup write the outputs
     if (p->S > 0) n += step_launch_count(*p);
+    if (p->S > 0 && p->f32_split_step) n += 1;   // R split into bf16 planes
   }
   info->launches = n;
   info->step_launches = (p->B > 0 && p->S > 0) ? step_launch_count(*p) : 0;
@@ -339,10 +360,11 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* st = static_cast<char*>(state_scratch);
-  const bool pers = p.engine == RNN_ENGINE_PERSISTENT;
+  const bool pers = p.engine == RNN_ENGINE_PERSISTENT && !p.pers_mfma;   // the small-batch persistent engine
   float* hbuf = pers ? nullptr : reinterpret_cast<float*>(st + p.st.hbuf);
   float* cstate = pers ? nullptr : reinterpret_cast<float*>(st + p.st.cell);
-  int* status = pers ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
+  int* status = (pers || p.pers_mfma) ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
+  int* flags = p.pers_mfma ? reinterpret_cast<int*>(st + p.st.flags) : nullptr;
 
   // -- state setup (slot 0 of the state, the cell state, the exchange words)
   SetupArgs sa{};
@@ -362,6 +384,8 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.xch2 = (pers && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
                 ? reinterpret_cast<unsigned long long*>(st + p.st.xch2) : nullptr;
   sa.status = status;
+  sa.flags = flags;
+  sa.nflags = flags ? kPersistentMfmaTiles : 0;
   if (!pers) {
     sa.Y = const_cast<char*>(Y);
     sa.Y_h = const_cast<char*>(Yh);
@@ -450,7 +474,14 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
       const bool mfma = mfma_step_supported(p);
       if (p.f32_split_step && (e = launch_split_r(R, rsplit, int64_t(p.D) * p.G * p.H * p.H, s)) != hipSuccess)
         return fail(RNN_ERR_HIP, cell, "R split launch: %s", hipGetErrorString(e));
-      for (int step = 0; step < int(p.steps); ++step)
+      bool done = false;
+      if (p.pers_mfma) {
+        e = launch_step_mfma_persistent(a, p, flags, status, s);
+        if (e != hipSuccess && e != hipErrorNotSupported)
+          return fail(RNN_ERR_HIP, cell, "persistent matrix-core step launch: %s", hipGetErrorString(e));
+        done = e == hipSuccess;   // not supported (R's alignment, epilogue planes): one launch per step
+      }
+      for (int step = 0; !done && step < int(p.steps); ++step)
         if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
           return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));
     }

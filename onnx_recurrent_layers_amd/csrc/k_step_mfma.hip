@@ -474,28 +474,44 @@ static hipError_t launch_h16(const MfmaStepArgs& m, int H, int B, int D, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s) {
+// Arguments of phase `ph` of a step (a GRU with linear_before_reset = 0 has
+// two: z and r, then the candidate) and the tile's batch rows.
+static MfmaStepArgs phase_args(const StepArgs& a, const Problem& p, int step, int ph, int* bm) {
   const bool skip_f = a.cell == RNN_CELL_LSTM && a.input_forget;
   const bool two_phase = a.cell == RNN_CELL_GRU && !a.lbr;
+  MfmaStepArgs m{};
+  m.a = a;
+  m.step = step;
+  m.phase = ph;
+  int gi = 0;
+  for (int g = 0; g < a.G; ++g) {
+    if (skip_f && g == 2) continue;
+    if (two_phase && ph == 0 && g == 2) continue;
+    if (two_phase && ph == 1 && g != 2) continue;
+    m.gate_of[gi++] = g;
+  }
+  m.Gp = gi;
+  int uj = 16;
+  *bm = 16;
+  mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), bm, &uj);
+  m.UJ = uj;
+  return m;
+}
+
+// Mode of the matrix-core step: 2 (f32 on the bf16 matrix cores, chosen when
+// the problem is created), 1 (f16 tensors, default activations), 0 (f32).
+static int step_mode(const Problem& p) {
+  return p.f32_split_step ? 2 : (p.desc.dtype == RNN_DTYPE_F16 && p.def_acts) ? 1 : 0;
+}
+
+hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s) {
+  const bool two_phase = a.cell == RNN_CELL_GRU && !a.lbr;
   for (int ph = 0; ph < (two_phase ? 2 : 1); ++ph) {
-    MfmaStepArgs m{};
-    m.a = a;
-    m.step = step;
-    m.phase = ph;
-    int gi = 0;
-    for (int g = 0; g < a.G; ++g) {
-      if (skip_f && g == 2) continue;
-      if (two_phase && ph == 0 && g == 2) continue;
-      if (two_phase && ph == 1 && g != 2) continue;
-      m.gate_of[gi++] = g;
-    }
-    m.Gp = gi;
-    int bm = 16, uj = 16;
-    mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
-    m.UJ = uj;
+    int bm = 16;
+    const MfmaStepArgs m = phase_args(a, p, step, ph, &bm);
     hipError_t e;
     const bool h16 = a.dtype == RNN_DTYPE_F16 && p.def_acts;
-    const int mode = p.f32_split_step ? 2 : h16 ? 1 : 0;
+    const int mode = step_mode(p);
     if (mode == 2 || ((h16 || a.dtype == RNN_DTYPE_F32) && step_dma_supported(a, mode))) {
       e = launch_step_dma(m, bm, mode, s);
     } else if (h16) {
@@ -511,6 +527,41 @@ hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipSt
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// The persistent form of the matrix-core step takes a problem when the
+// direct-to-LDS kernel takes its shape in its mode and the tiles fit the chip
+// one workgroup per compute unit (its LDS allows no more).  R's alignment is
+// only known at encode time: launch_step_mfma_persistent reports
+// hipErrorNotSupported when it rules the kernel out, and the caller then
+// launches per step.
+bool mfma_persistent_supported(const Problem& p, int* tiles_out) {
+  if (!mfma_step_supported(p) || p.S < 1 || p.steps < 1) return false;
+  const int mode = step_mode(p);
+  if (mode == 0 && p.desc.dtype == RNN_DTYPE_F16) return false;   // f16 R widened: the register-staged kernel
+  StepArgs t{};
+  t.G = p.G;
+  t.D = p.D;
+  t.H = int(p.H);
+  t.B = int(p.B);
+  if (!step_dma_supported(t, mode)) return false;
+  const bool skip_f = p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget;
+  int bm = 16, uj = 16;
+  mfma_tile(int(p.B), int(p.H), p.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
+  const int64_t tiles = ((p.H + uj - 1) / uj) * ((p.B + bm - 1) / bm) * p.D;
+  if (tiles > kPersistentMfmaTiles) return false;
+  *tiles_out = int(tiles);
+  return true;
+}
+
+hipError_t launch_step_mfma_persistent(const StepArgs& a, const Problem& p, int* flags, int* status, hipStream_t s) {
+  const int mode = step_mode(p);
+  if (mode != 2 && !step_dma_supported(a, mode)) return hipErrorNotSupported;
+  const int P = (a.cell == RNN_CELL_GRU && !a.lbr) ? 2 : 1;
+  MfmaStepArgs ph[2];
+  int bm = 16;
+  for (int k = 0; k < P; ++k) ph[k] = phase_args(a, p, 0, k, &bm);
+  return launch_step_dma_persistent(ph, P, bm, mode, flags, status, s);
 }
 
 }  // namespace rnnhip

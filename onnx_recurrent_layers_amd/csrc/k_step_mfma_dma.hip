@@ -33,6 +33,8 @@
 // The k index is permuted inside a chunk (lane group q of an operand takes a
 // contiguous quarter of the chunk), identically for h and R, so each lane
 // reads whole 16-byte segments; a sum over a permuted k range is the same sum.
+#include <cstdlib>
+
 #include "step_mfma.h"
 
 namespace rnnhip {
@@ -135,6 +137,7 @@ struct EpiCtx {
   float clip;
   int H, B, GH, s, cell, lbr, phase, input_forget, has_p, rev, Gp;
   int S, D, d, layout;
+  bool coh;             // persistent launch: state read and written at device scope
   int gate[4];
   Act act[3];
 };
@@ -145,13 +148,14 @@ __device__ __forceinline__ float uniform(float v) {
 }
 
 template <typename RT>
-__device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
+__device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d, int step, bool coh) {
   const StepArgs& a = m.a;
   EpiCtx c;
   c.H = a.H;
   c.B = a.B;
   c.GH = a.G * a.H;
-  c.s = m.step;
+  c.s = step;
+  c.coh = coh;
   c.cell = a.cell;
   c.lbr = a.lbr;
   c.phase = m.phase;
@@ -171,8 +175,8 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
   }
   const int64_t DBH = int64_t(a.D) * a.B * a.H, dBH = int64_t(d) * a.B * a.H;
   c.xw = a.xw + int64_t(d) * a.S * a.B * c.GH;
-  c.hprev = a.hbuf + int64_t(m.step & 1) * DBH + dBH;
-  c.hnext = a.hbuf + int64_t((m.step + 1) & 1) * DBH + dBH;
+  c.hprev = a.hbuf + int64_t(step & 1) * DBH + dBH;
+  c.hnext = a.hbuf + int64_t((step + 1) & 1) * DBH + dBH;
   c.Y = a.Y;
   c.Y_h = a.Y_h;
   c.Y_c = a.Y_c;
@@ -182,7 +186,7 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
   c.layout = a.layout;
   c.cst = a.cell_state + dBH;
   c.DBH = DBH;
-  c.hsn = a.hsplit ? a.hsplit + int64_t((m.step + 1) & 1) * 2 * DBH + dBH : nullptr;
+  c.hsn = a.hsplit ? a.hsplit + int64_t((step + 1) & 1) * 2 * DBH + dBH : nullptr;
   c.rhs = a.rhsplit ? a.rhsplit + dBH : nullptr;
   c.zbuf = a.zbuf + dBH;
   c.rhbuf = a.rhbuf + dBH;
@@ -191,6 +195,31 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d) {
   c.bias = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(bias), 0, bias ? 2 * c.GH * int(sizeof(RT)) : 0, kRsrcWord3);
   c.peep = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(P), 0, P ? 3 * a.H * int(sizeof(RT)) : 0, kRsrcWord3);
   return c;
+}
+
+// State that a launch both writes and reads (h, c, z, r*h and their bf16
+// planes).  In a persistent launch it goes through device scope (cache
+// policy sc1): other workgroups, on other XCDs, read h between steps, and a
+// workgroup's own values come back to it through caches that other traffic
+// went through.  A per-step launch needs nothing of the kind: kernel
+// boundaries order and publish everything.
+__device__ __forceinline__ float st_ld(const float* p, bool coh) {
+  return coh ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+}
+__device__ __forceinline__ void st_st(float* p, float v, bool coh) {
+  if (coh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+__device__ __forceinline__ void st_split(unsigned short* p, int64_t plane, float v, bool coh) {
+  unsigned short hi, lo;
+  split_bf16_bits(v, hi, lo);
+  if (coh) {
+    __hip_atomic_store(p, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + plane, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    p[0] = hi;
+    p[plane] = lo;
+  }
 }
 
 // f16 elements are loaded as the aligned dword that holds them (the vectors
@@ -243,17 +272,17 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
     o.xv[gi] = xw[c.gate[gi] * H + j];
   }
   if (c.cell == RNN_CELL_LSTM) {
-    o.cprev = c.cst[si];
+    o.cprev = st_ld(c.cst + si, c.coh);
   } else if (c.cell == RNN_CELL_GRU) {
-    o.hprev = c.hprev[si];
-    if (!c.lbr && c.phase == 1) o.z = c.zbuf[si];
+    o.hprev = st_ld(c.hprev + si, c.coh);
+    if (!c.lbr && c.phase == 1) o.z = st_ld(c.zbuf + si, c.coh);
   }
 }
 
 // h of the next step: f32, and in mode 2 also its bf16 planes.
 __device__ __forceinline__ void epi_put_h(const EpiCtx& c, int64_t si, float h) {
-  c.hnext[si] = h;
-  if (c.hsn) split_bf16_bits(h, c.hsn[si], c.hsn[c.DBH + si]);
+  st_st(c.hnext + si, h, c.coh);
+  if (c.hsn) st_split(c.hsn + si, c.DBH, h, c.coh);
 }
 
 // Y of one finished element and, after its row's last step, Y_h / Y_c.
@@ -302,7 +331,7 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
       lstm_unit<DEF>(p4, pp, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
     else
       lstm_unit<DEF>(p4, nullptr, o.cprev, c.clip, c.input_forget, acts, &h, &cc);
-    c.cst[si] = cc;
+    st_st(c.cst + si, cc, c.coh);
     epi_put_h(c, si, h);
     epi_outputs<RT>(c, b, j, o.len, h, cc);
   } else if (c.cell == RNN_CELL_GRU) {
@@ -317,10 +346,10 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
     } else if (c.phase == 0) {
       const float z = gru_gate<DEF>(pre(0), c.clip, acts);
       const float rg = gru_gate<DEF>(pre(1), c.clip, acts);
-      c.zbuf[si] = z;
+      st_st(c.zbuf + si, z, c.coh);
       const float rh = rg * o.hprev;
-      c.rhbuf[si] = rh;
-      if (c.rhs) split_bf16_bits(rh, c.rhs[si], c.rhs[c.DBH + si]);
+      st_st(c.rhbuf + si, rh, c.coh);
+      if (c.rhs) st_split(c.rhs + si, c.DBH, rh, c.coh);
     } else {
       // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
       const float h = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
@@ -368,10 +397,17 @@ __device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s
                                          RNN_LDS_PTR(dst + gi * n_el), 4, 0, 0);
     if (ns > 0) {
       const float* st = c.cell == RNN_CELL_LSTM ? c.cst : c.hprev;
-      __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(st + si), RNN_LDS_PTR(dst + c.Gp * n_el), 4, 0, 0);
+      if (c.coh)
+        __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(st + si), RNN_LDS_PTR(dst + c.Gp * n_el), 4, 0, 16);
+      else
+        __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(st + si), RNN_LDS_PTR(dst + c.Gp * n_el), 4, 0, 0);
     }
-    if (ns > 1)
-      __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(c.zbuf + si), RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 4, 0, 0);
+    if (ns > 1) {
+      if (c.coh)
+        __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(c.zbuf + si), RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 4, 0, 16);
+      else
+        __builtin_amdgcn_global_load_lds(RNN_GLOBAL_PTR(c.zbuf + si), RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 4, 0, 0);
+    }
   }
 }
 
@@ -400,8 +436,10 @@ __device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& fi
   }
 }
 
-template <int MODE, int BM, int CB>
-__global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
+// One step (one phase of a two-phase GRU step) of one tile, run by a
+// per-step launch (PERS = false) or inside the persistent kernel below.
+template <int MODE, int BM, int CB, bool PERS>
+__device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   typedef DmaCfg<MODE, BM, CB> C;
   typedef typename C::Geo Geo;
   typedef typename Geo::RT RT;
@@ -420,7 +458,6 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
 
   const StepArgs& a = m.a;
   const int H = a.H, B = a.B, G = a.G, S = a.S;
-  const int s = m.step;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = blockIdx.x * m.UJ;
   const int b0 = blockIdx.y * BM;
@@ -483,6 +520,7 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
       brow[cb][i] = ok ? unsigned(gate_block(m, gi) * H + j0 + u) * unsigned(H) * BES : kOutOfRange;
     }
   auto slot = [&](int i) -> unsigned char* { return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3; };
+  const int nk = (H + KC - 1) / KC;
   auto fetch = [&](int kc, unsigned char* st) {
     const int k0 = kc * KC;
 #pragma unroll
@@ -496,7 +534,8 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
         const int k = k0 + aseg[i] * 4;
         off = k < H ? arow[i] + unsigned(k) * 4u : kOutOfRange;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, RNN_LDS_PTR(st + (wave * LA + i) * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, RNN_LDS_PTR(st + (wave * LA + i) * 1024), 16, off, 0, 0,
+                                               PERS ? 16 : 0);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -521,7 +560,6 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
   int lv = 0;
   if (wave == 0 && lane < BM && b0 + lane < B) lv = a.lens ? a.lens[b0 + lane] : S;
 
-  const int nk = (H + KC - 1) / KC;
 #pragma unroll
   for (int c = 0; c < NS - 1; ++c) fetch(c, slot(c));
 
@@ -552,7 +590,7 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     return;
   }
-  const EpiCtx ctx = epi_context<RT>(m, d);
+  const EpiCtx ctx = epi_context<RT>(m, d, s, PERS);
   const int n_el = BM * UJ;   // a multiple of the workgroup size
   EpiIn first;
   epi_gather<RT>(ctx, len_s, tid, n_el, ujs, b0, j0, first);
@@ -696,6 +734,69 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
 }
 
 template <int MODE, int BM, int CB>
+__global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
+  dma_step<MODE, BM, CB, false>(m, m.step);
+}
+
+// Every step in one cooperative launch (all tiles resident together).  A
+// workgroup keeps its tile for the whole layer, so the R rows it streams stay
+// in its XCD's L2 from one step to the next instead of being fetched again
+// after each kernel boundary.  Between phases, each workgroup publishes the
+// count of phases it has finished in its own flag (a device-scope store after
+// all its state stores have completed) and waits until every workgroup of its
+// batch tile and direction, the ones whose h rows it reads, has published the
+// count it needs.  Those are also the only readers of the h rows it writes,
+// so a slot of h is never rewritten while a reader still needs it.  Every
+// wait has a safety bound: a stuck run sets the status word and ends.
+struct PersDmaArgs {
+  MfmaStepArgs ph[2];   // per phase (a GRU with linear_before_reset = 0 has two)
+  int P;                // phases per step
+  int* flags;           // one per workgroup: phases finished; zeroed by the state setup
+  int* status;          // set to 1 if a wait ran past its bound
+};
+
+constexpr long kFlagSpinLimit = 1l << 22;
+
+template <int MODE, int BM, int CB>
+__global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p) {
+  __shared__ int abort_s;
+  const int gx = int(gridDim.x);
+  const int row = int(blockIdx.y + gridDim.y * blockIdx.z);   // batch tile and direction
+  const int me = int(blockIdx.x) + gx * row;
+  const int* peers = p.flags + gx * row;
+  const int steps = p.ph[0].a.steps, P = p.P;
+  if (threadIdx.x == 0) abort_s = 0;
+  __syncthreads();
+  for (int s = 0; s < steps; ++s)
+    for (int ph = 0; ph < P; ++ph) {
+      const int want = s * P + ph;
+      if (want > 0) {
+        if (threadIdx.x < 64) {
+          for (int x = int(threadIdx.x); x < gx; x += 64) {
+            long spin = 0;
+            while (__hip_atomic_load(peers + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want)
+              if (++spin > kFlagSpinLimit) {
+                abort_s = 1;
+                break;
+              }
+          }
+        }
+        __syncthreads();
+        if (abort_s) {
+          if (threadIdx.x == 0) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+      }
+      if (ph == 0) dma_step<MODE, BM, CB, true>(p.ph[0], s);
+      else dma_step<MODE, BM, CB, true>(p.ph[1], s);
+      // every state store of this workgroup has completed before the flag
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(p.flags + me, want + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int MODE, int BM, int CB>
 static hipError_t launch_cfg(const MfmaStepArgs& m, hipStream_t s) {
   const StepArgs& a = m.a;
   const dim3 grid(unsigned((a.H + m.UJ - 1) / m.UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
@@ -714,6 +815,67 @@ static hipError_t launch_bm(const MfmaStepArgs& m, hipStream_t s) {
   if (ncb <= 4 && planes <= DmaCfg<MODE, BM, 1>::STAGE) return launch_cfg<MODE, BM, 1>(m, s);
   if (planes > DmaCfg<MODE, BM, 2>::STAGE) return hipErrorInvalidValue;
   return launch_cfg<MODE, BM, 2>(m, s);
+}
+
+// The persistent form: one column split for both phases (the wider one).
+template <int MODE, int BM, int CB>
+static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
+  const StepArgs& a = pa.ph[0].a;
+  const dim3 grid(unsigned((a.H + pa.ph[0].UJ - 1) / pa.ph[0].UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
+  auto kern = step_dma_pers_kernel<MODE, BM, CB>;
+  PersDmaArgs arg = pa;
+  // RNN_PLAIN_LAUNCH=1: the same grid without the cooperative API, after a
+  // host check that every workgroup fits on the chip at once (for profilers
+  // that fail on cooperative launches)
+  static const bool plain = [] {
+    const char* e = std::getenv("RNN_PLAIN_LAUNCH");
+    return e && e[0] == '1';
+  }();
+  if (plain) {
+    int per_cu = 0, dev = 0, cus = 0;
+    hipError_t e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kMThreads,
+                                                           0)) != hipSuccess)
+      return e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if (int64_t(per_cu) * cus < int64_t(grid.x) * grid.y * grid.z) return hipErrorCooperativeLaunchTooLarge;
+    hipLaunchKernelGGL(kern, grid, dim3(kMThreads), 0, s, arg);
+    return hipGetLastError();
+  }
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), grid, dim3(kMThreads), args, 0u, s);
+}
+
+template <int MODE, int BM>
+static hipError_t launch_pers_bm(const PersDmaArgs& pa, hipStream_t s) {
+  bool two = false;
+  for (int ph = 0; ph < pa.P; ++ph) {
+    const MfmaStepArgs& m = pa.ph[ph];
+    const int ncb = (m.Gp * m.UJ) >> 4;
+    const int planes = (m.Gp + epi_state_planes(m.a.cell, m.a.lbr, m.phase)) * BM * m.UJ * 4;
+    if (ncb > 4 || planes > DmaCfg<MODE, BM, 1>::STAGE) two = true;
+    if (planes > DmaCfg<MODE, BM, 2>::STAGE) return hipErrorNotSupported;
+  }
+  return two ? launch_pers_cfg<MODE, BM, 2>(pa, s) : launch_pers_cfg<MODE, BM, 1>(pa, s);
+}
+
+hipError_t launch_step_dma_persistent(const MfmaStepArgs* ph, int P, int bm, int mode, int* flags, int* status,
+                                      hipStream_t s) {
+  PersDmaArgs pa{};
+  pa.ph[0] = ph[0];
+  pa.ph[1] = P > 1 ? ph[1] : ph[0];
+  pa.P = P;
+  pa.flags = flags;
+  pa.status = status;
+  if (mode == 1)
+    return bm == 64 ? launch_pers_bm<1, 64>(pa, s) : bm == 32 ? launch_pers_bm<1, 32>(pa, s)
+                                                      : launch_pers_bm<1, 16>(pa, s);
+  if (mode == 2)
+    return bm == 64 ? launch_pers_bm<2, 64>(pa, s) : bm == 32 ? launch_pers_bm<2, 32>(pa, s)
+                                                      : launch_pers_bm<2, 16>(pa, s);
+  return bm == 64 ? launch_pers_bm<0, 64>(pa, s) : bm == 32 ? launch_pers_bm<0, 32>(pa, s)
+                                                    : launch_pers_bm<0, 16>(pa, s);
 }
 
 bool step_dma_supported(const StepArgs& a, int mode) {

@@ -31,6 +31,7 @@ struct StateLayout {
   size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
   size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
   size_t status;   // int: persistent engine status (1: a wait hit its safety bound)
+  size_t flags;    // int per workgroup of the persistent matrix-core step: phases finished
   size_t total;
 };
 
@@ -50,6 +51,8 @@ struct Problem {
   int pers_blocks = 0;       // workgroups of the cooperative launch
   int pers_units = 0;        // units per workgroup
   int pers_wg_per_dir = 0;
+  // the persistent engine in its matrix-core form (batches of 16 and more)
+  bool pers_mfma = false;
   // f32 tensors: the projection on the bf16 matrix cores (three split
   // products) instead of the f32 matrix cores
   bool f32_split_proj = false;
@@ -115,6 +118,8 @@ struct SetupArgs {
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
   int* status;               // persistent engine status word, or null
+  int* flags;                // workgroup flags of the persistent matrix-core step, zeroed here, or null
+  int nflags;
   // outputs no step of the per-step engine writes (null for the persistent
   // engine, which writes them itself): Y past each row's length, the final
   // states of rows of length 0, and every final state when Seq = 0
@@ -142,6 +147,11 @@ hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);
 bool mfma_step_supported(const Problem& p);
+// Persistent form of the matrix-core step: one cooperative launch for every
+// step, at most kPersistentMfmaTiles workgroups (one per compute unit).
+constexpr int kPersistentMfmaTiles = 256;
+bool mfma_persistent_supported(const Problem& p, int* tiles);
+hipError_t launch_step_mfma_persistent(const StepArgs& a, const Problem& p, int* flags, int* status, hipStream_t s);
 // Whether the direct-to-LDS matrix-core step takes this shape in a mode (0:
 // f32 on the f32 matrix cores, 1: f16 with split h, 2: f32 on the bf16 matrix
 // cores).

@@ -262,6 +262,46 @@ def test_matrix_step_bf16x3(cell, direction, layout, opt, B, H, tile, acts, monk
     check(spec, inp, engine="launch", what=f"bf16x3 step {cell}/{direction}/L{layout}/opt{opt}/B{B}/H{H}/{tile}")
 
 
+# The persistent form of the matrix-core step (one cooperative launch for
+# every step, batches of 16 and more): the three modes, every cell, both GRU
+# forms (two phases per step), forced tile shapes and column splits, ragged
+# batch and hidden sizes, lengths with 0, both layouts and directions.
+PERS_MFMA_CASES = [
+    # cell, dtype, direction, layout, option, B, H, tile, split
+    ("LSTM", "f16", "forward", 1, 1, 64, 128, None, None),
+    ("LSTM", "f16", "bidirectional", 0, 0, 37, 136, "32x32", None),
+    ("GRU", "f16", "bidirectional", 1, 0, 70, 136, "64x32", None),
+    ("GRU", "f16", "reverse", 0, 1, 20, 256, "16x16", None),
+    ("RNN", "f16", "forward", 0, 0, 33, 520, "64x64", None),
+    ("LSTM", "f32", "bidirectional", 0, 0, 37, 64, "16x16", "0"),
+    ("GRU", "f32", "forward", 1, 0, 17, 96, "64x16", "0"),
+    ("RNN", "f32", "reverse", 0, 0, 40, 72, None, "0"),
+    ("LSTM", "f32", "reverse", 1, 1, 40, 136, "32x32", "1"),
+    ("GRU", "f32", "bidirectional", 0, 0, 70, 136, "64x32", "1"),
+    ("GRU", "f32", "forward", 0, 1, 20, 256, "32x16", "1"),
+    ("RNN", "f32", "bidirectional", 1, 0, 33, 520, "64x64", "1"),
+]
+
+
+@pytest.mark.parametrize("cell,dtype,direction,layout,opt,B,H,tile,split", PERS_MFMA_CASES,
+                         ids=["-".join(map(str, c)) for c in PERS_MFMA_CASES])
+def test_persistent_matrix_step(cell, dtype, direction, layout, opt, B, H, tile, split, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    if tile:
+        monkeypatch.setenv("RNN_MFMA_TILE", tile)
+    if split:
+        monkeypatch.setenv("RNN_F32_SPLIT", split)
+    spec = LayerSpec(cell, seq=9, batch=B, input=40, hidden=H, direction=direction, layout=layout, dtype=dtype,
+                     linear_before_reset=opt if cell == "GRU" else 0, input_forget=opt if cell == "LSTM" else 0,
+                     init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM", clip=2.0,
+                     outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    inp = make_inputs(spec, 53, Dists(sequence_lens=("I", 0, 9), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    check(spec, inp, engine="persistent", what=f"persistent mfma {cell}/{dtype}/{direction}/L{layout}/opt{opt}/"
+                                                 f"B{B}/H{H}/{tile}/split{split}")
+
+
 def test_large_batch_general_activations():
     """The matrix-core step kernel with non-default activations (f16 tensors
     then take the f32 path, f32 tensors always do)."""
@@ -347,7 +387,7 @@ def test_batch_above_eight_and_hidden_not_dividing(engine):
 # the five seeded workloads at full size
 # ---------------------------------------------------------------------------
 FULL = [("C1", {}), ("C2", {}), ("C3", {"linear_before_reset": 0}), ("C3", {"linear_before_reset": 1}),
-        ("C4", {}), ("C5", {})]
+        ("C4", {}), ("C5", {}), ("C4", {"engine": "launch"}), ("C5", {"engine": "persistent"})]
 SAMPLE_ROWS = {"C4": [0, 9, 31, 63], "C5": [0, 255]}
 
 
@@ -373,10 +413,17 @@ def test_engine_choice_and_plan():
         layer = rl.Layer(spec, engine="auto", device="cuda:0")
         assert layer.plan.engine == rl.ENGINES["persistent"], name
         assert layer.plan.step_launches == 1
-    for name in ("C4", "C5"):
-        spec, _ = synth.config(name)
-        layer = rl.Layer(spec, engine="auto", device="cuda:0")
-        assert layer.plan.engine == rl.ENGINES["launch"], name
+    # C4 (f16, split h): the matrix-core step in one cooperative launch; C5
+    # (f32): one launch per step, unless the persistent engine is asked for
+    spec, _ = synth.config("C4")
+    layer = rl.Layer(spec, engine="auto", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"]
+    assert layer.plan.step_launches == 1 and layer.plan.step_blocks == 256
+    spec, _ = synth.config("C5")
+    layer = rl.Layer(spec, engine="auto", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["launch"] and layer.plan.step_launches == 1024
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_blocks == 256
 
 
 @pytest.mark.parametrize("name,over", FULL + [("C2", {"engine": "launch"}), ("C3", {"engine": "launch"})],
