@@ -187,6 +187,21 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     return bad(RNN_ERR_UNSUPPORTED, "engine: the persistent engine does not take this shape");
   p->engine = engine;
   p->pers_mfma = engine == RNN_ENGINE_PERSISTENT && !pers_ok;
+  // h as 16-bit halves for the matrix-core step: bf16 with the bf16 mode;
+  // f16 for f16 layers with the default activations whose rows are whole
+  // 16-byte segments (the direct-to-LDS kernel's f16 mode; whether it runs is
+  // settled at encode time by R's alignment, and the planes are written in
+  // any case)
+  if (p->f32_split_step) {
+    p->h_split = 2;
+  } else if (!pers_ok && mfma_step_supported(*p) && desc->dtype == RNN_DTYPE_F16 && p->def_acts) {
+    StepArgs t{};
+    t.G = p->G;
+    t.D = p->D;
+    t.H = int(p->H);
+    t.B = int(p->B);
+    if (step_dma_supported(t, 1)) p->h_split = 1;
+  }
   if (p->pers_mfma) p->pers_blocks = mfma_tiles;
   // f32 projections of 2^32 flops and more run as three bf16 products (the
   // f32 matrix cores have a sixteenth of the bf16 rate); RNN_F32_SPLIT=0 or 1
@@ -214,6 +229,8 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
     if (p->f32_split_step) {
       st.rsplit = off;  off = align256(off + 2 * size_t(p->D) * size_t(GH) * size_t(p->H) * 2);
+    }
+    if (p->h_split) {
       st.hsplit = off;  off = align256(off + 4 * size_t(dbh) * 2);
       st.rhsplit = off; off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 2 : 0));
     }
@@ -377,8 +394,9 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.init_c = ic;
   sa.hbuf = hbuf;
   unsigned short* rsplit = p.f32_split_step ? reinterpret_cast<unsigned short*>(st + p.st.rsplit) : nullptr;
-  unsigned short* hsplit = p.f32_split_step ? reinterpret_cast<unsigned short*>(st + p.st.hsplit) : nullptr;
+  unsigned short* hsplit = p.h_split ? reinterpret_cast<unsigned short*>(st + p.st.hsplit) : nullptr;
   sa.hsplit = hsplit;
+  sa.split_kind = p.h_split;
   sa.cell_state = cstate;
   sa.xch = pers ? reinterpret_cast<unsigned long long*>(st + p.st.xch) : nullptr;
   sa.xch2 = (pers && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
@@ -414,8 +432,9 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   a.hbuf = hbuf;
   a.rsplit = rsplit;
   a.hsplit = hsplit;
-  a.rhsplit = (p.f32_split_step && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
+  a.rhsplit = (p.h_split && cell == RNN_CELL_GRU && !p.desc.linear_before_reset)
                   ? reinterpret_cast<unsigned short*>(st + p.st.rhsplit) : nullptr;
+  a.split_kind = p.h_split;
   a.Y = const_cast<char*>(Y);
   a.Y_h = const_cast<char*>(Yh);
   a.Y_c = const_cast<char*>(Yc);

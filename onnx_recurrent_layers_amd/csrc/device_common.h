@@ -90,6 +90,19 @@ __device__ __forceinline__ void split_bf16_bits(float x, unsigned short& hi, uns
   lo = __builtin_bit_cast(unsigned short, __bf16(x - float(h)));
 }
 
+// The same split into f16 halves: hi = f16(x), lo = f16(x - hi).
+__device__ __forceinline__ void split_f16_bits(float x, unsigned short& hi, unsigned short& lo) {
+  const _Float16 h = _Float16(x);
+  hi = __builtin_bit_cast(unsigned short, h);
+  lo = __builtin_bit_cast(unsigned short, _Float16(x - float(h)));
+}
+
+// kind 1: f16 halves; kind 2: bf16 halves.
+__device__ __forceinline__ void split_bits(int kind, float x, unsigned short& hi, unsigned short& lo) {
+  if (kind == 1) split_f16_bits(x, hi, lo);
+  else split_bf16_bits(x, hi, lo);
+}
+
 // Index of output Y at time t, direction d, batch row b, unit j:
 // layout 0 [S][D][B][H], layout 1 [B][S][D][H].
 __device__ __forceinline__ int64_t y_index(int layout, int S, int D, int B, int H, int t, int d, int b, int j) {
@@ -122,7 +135,7 @@ __device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int pa
     const float h0 = a.init_h ? ld(static_cast<const T*>(a.init_h), src) : 0.f;
     const float c0 = a.init_c ? ld(static_cast<const T*>(a.init_c), src) : 0.f;
     if (a.hbuf) a.hbuf[i] = h0;
-    if (a.hsplit) split_bf16_bits(h0, a.hsplit[i], a.hsplit[DBH + i]);
+    if (a.hsplit) split_bits(a.split_kind, h0, a.hsplit[i], a.hsplit[DBH + i]);
     if (a.cell_state) a.cell_state[i] = c0;
     if (a.xch) {
       // word = (tag << 32) | value bits; slot 0 carries step 0, slot 1 no step yet.

@@ -9,9 +9,10 @@
 // those units (product tile [BM] x [Gp*UJ], K = H), and finishes the gate
 // arithmetic itself.  Three modes:
 //   mode 0, f32 tensors: v_mfma_f32_16x16x4_f32 on f32 h and f32 R;
-//   mode 1, f16 tensors with the default activations: h split into
-//     hi = f16(h) and lo = f16(h - hi), R.hi + R.lo on v_mfma_f32_16x16x32_f16
-//     with separate f32 accumulators (f16 products are exact in f32);
+//   mode 1, f16 tensors with the default activations: h as f16 halves
+//     hi = f16(h) and lo = f16(h - hi) (written by the step that produced h),
+//     R.hi + R.lo on v_mfma_f32_16x16x32_f16 with separate f32 accumulators
+//     (f16 products are exact in f32);
 //   mode 2, large f32 layers: h and R as bf16 hi/lo planes (R split once per
 //     layer, h by the step that produces it), each product taken as
 //     lo_h.hi_R + hi_h.lo_R + hi_h.hi_R on v_mfma_f32_16x16x32_bf16 with one
@@ -69,10 +70,10 @@ template <> struct DmaGeo<0> {           // f32 h, f32 R
   static constexpr int ASEGS = 16;       // 16-byte segments per h row of a chunk
   static constexpr int BELEMS = 4;       // R elements per segment
 };
-template <> struct DmaGeo<1> {           // f32 h split on the fly, f16 R
+template <> struct DmaGeo<1> {           // f16 halves of h, f16 R
   typedef half_t RT;
   static constexpr int KC = 128;
-  static constexpr int ASEGS = 32;
+  static constexpr int ASEGS = 32;       // a row of a chunk: 16 hi segments, then 16 lo segments
   static constexpr int BELEMS = 8;
 };
 template <> struct DmaGeo<2> {           // bf16 hi/lo planes of h and R (f32 tensors)
@@ -138,6 +139,7 @@ struct EpiCtx {
   int H, B, GH, s, cell, lbr, phase, input_forget, has_p, rev, Gp;
   int S, D, d, layout;
   bool coh;             // persistent launch: state read and written at device scope
+  int split_kind;       // of hsn / rhs: 1 f16 halves, 2 bf16 halves
   int gate[4];
   Act act[3];
 };
@@ -188,6 +190,7 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d, int 
   c.DBH = DBH;
   c.hsn = a.hsplit ? a.hsplit + int64_t((step + 1) & 1) * 2 * DBH + dBH : nullptr;
   c.rhs = a.rhsplit ? a.rhsplit + dBH : nullptr;
+  c.split_kind = a.split_kind;
   c.zbuf = a.zbuf + dBH;
   c.rhbuf = a.rhbuf + dBH;
   const RT* bias = a.bias ? static_cast<const RT*>(a.bias) + int64_t(d) * 2 * c.GH : nullptr;
@@ -210,9 +213,9 @@ __device__ __forceinline__ void st_st(float* p, float v, bool coh) {
   if (coh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
 }
-__device__ __forceinline__ void st_split(unsigned short* p, int64_t plane, float v, bool coh) {
+__device__ __forceinline__ void st_split(unsigned short* p, int64_t plane, float v, bool coh, int kind) {
   unsigned short hi, lo;
-  split_bf16_bits(v, hi, lo);
+  split_bits(kind, v, hi, lo);
   if (coh) {
     __hip_atomic_store(p, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(p + plane, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -282,7 +285,7 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
 // h of the next step: f32, and in mode 2 also its bf16 planes.
 __device__ __forceinline__ void epi_put_h(const EpiCtx& c, int64_t si, float h) {
   st_st(c.hnext + si, h, c.coh);
-  if (c.hsn) st_split(c.hsn + si, c.DBH, h, c.coh);
+  if (c.hsn) st_split(c.hsn + si, c.DBH, h, c.coh, c.split_kind);
 }
 
 // Y of one finished element and, after its row's last step, Y_h / Y_c.
@@ -349,7 +352,7 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
       st_st(c.zbuf + si, z, c.coh);
       const float rh = rg * o.hprev;
       st_st(c.rhbuf + si, rh, c.coh);
-      if (c.rhs) st_split(c.rhs + si, c.DBH, rh, c.coh);
+      if (c.rhs) st_split(c.rhs + si, c.DBH, rh, c.coh, c.split_kind);
     } else {
       // linear_before_reset = 0: h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
       const float h = gru_unit<DEF>(o.z, pre(0), o.hprev, c.clip, acts);
@@ -468,30 +471,34 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   const int64_t DBH = int64_t(a.D) * B * H;
   const int64_t dBH = int64_t(d) * B * H;
   const bool cand_phase = a.cell == RNN_CELL_GRU && !a.lbr && m.phase == 1;
-  // operand resources.  Mode 2 reads bf16 planes: the hi plane of this
-  // direction, with the lo plane `plane_a` (`plane_b`) bytes further on, and
-  // the resource reaching to the end of this direction's lo plane.
+  // operand resources.  Modes 1 and 2 read h as 16-bit planes: the hi plane
+  // of this direction, with the lo plane `plane_a` bytes further on, and the
+  // resource reaching to the end of this direction's lo plane; mode 2 reads
+  // R likewise (`plane_b`).
   __amdgpu_buffer_rsrc_t ra, rb;
   unsigned plane_a = 0, plane_b = 0;
-  if constexpr (MODE == 2) {
+  if constexpr (MODE >= 1) {
     const unsigned short* hs2 = cand_phase ? a.rhsplit + dBH : a.hsplit + int64_t(s & 1) * 2 * DBH + dBH;
-    const unsigned short* rs2 = a.rsplit + int64_t(d) * G * H * H;
     plane_a = unsigned(DBH) * 2u;
-    plane_b = unsigned(a.D) * unsigned(G) * unsigned(H) * unsigned(H) * 2u;
     ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(hs2), 0,
                                            int(plane_a + unsigned(B) * unsigned(H) * 2u), kRsrcWord3);
+  } else {
+    const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u),
+                                           kRsrcWord3);
+  }
+  if constexpr (MODE == 2) {
+    const unsigned short* rs2 = a.rsplit + int64_t(d) * G * H * H;
+    plane_b = unsigned(a.D) * unsigned(G) * unsigned(H) * unsigned(H) * 2u;
     rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(rs2), 0,
                                            int(plane_b + unsigned(G) * unsigned(H) * unsigned(H) * 2u), kRsrcWord3);
   } else {
-    const float* hsrc = cand_phase ? a.rhbuf + dBH : a.hbuf + int64_t(s & 1) * DBH + dBH;
     const RT* Rd = static_cast<const RT*>(a.R) + int64_t(d) * G * H * H;
-    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(hsrc), 0, int(unsigned(B) * unsigned(H) * 4u),
-                                           kRsrcWord3);
     rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<RT*>(Rd), 0,
                                            int(unsigned(G) * unsigned(H) * unsigned(H) * unsigned(sizeof(RT))),
                                            kRsrcWord3);
   }
-  constexpr unsigned AES = MODE == 2 ? 2u : 4u;              // bytes of an element of h as loaded
+  constexpr unsigned AES = MODE >= 1 ? 2u : 4u;              // bytes of an element of h as loaded
   constexpr unsigned BES = MODE == 2 ? 2u : unsigned(sizeof(RT));  // ... of R
 
   // h segments of this lane: load i of the wave fills LDS bytes
@@ -527,9 +534,10 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
     for (int i = 0; i < LA; ++i) {
       // a row outside the tile starts at the out-of-range marker, so row + k stays out of range
       unsigned off;
-      if constexpr (MODE == 2) {   // logical segment: plane (hi, lo) and 8-element k group
-        const int k = k0 + (aseg[i] & 7) * 8;
-        off = k < H ? arow[i] + (aseg[i] >> 3) * plane_a + unsigned(k) * 2u : kOutOfRange;
+      if constexpr (MODE >= 1) {   // logical segment: plane (hi, lo) and 8-element k group
+        constexpr int SPP = ASEGS / 2;   // segments of one plane
+        const int k = k0 + (aseg[i] % SPP) * 8;
+        off = k < H ? arow[i] + unsigned(aseg[i] / SPP) * plane_a + unsigned(k) * 2u : kOutOfRange;
       } else {
         const int k = k0 + aseg[i] * 4;
         off = k < H ? arow[i] + unsigned(k) * 4u : kOutOfRange;
@@ -670,21 +678,16 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
         for (int kk = 0; kk < 4; ++kk)
           bv[cb][kk] =
               *reinterpret_cast<const hx8*>(Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * q + kk) ^ r16) << 4));
+      // step kk takes the 8-element k group 4q + kk of both halves of h and
+      // of R (the same k for both operands)
       hx8 ah[NBI][4], al[NBI][4];
 #pragma unroll
       for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const unsigned char* row = st + (bi * 16 + r16) * 512;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(row + (((8 * q + 2 * kk) ^ r16) << 4));
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(row + (((8 * q + 2 * kk + 1) ^ r16) << 4));
-          const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-          for (int z = 0; z < 8; ++z) {
-            const half_t hi = half_t(x[z]);
-            ah[bi][kk][z] = hi;
-            al[bi][kk][z] = half_t(x[z] - float(hi));
-          }
+          ah[bi][kk] = *reinterpret_cast<const hx8*>(row + (((4 * q + kk) ^ r16) << 4));
+          al[bi][kk] = *reinterpret_cast<const hx8*>(row + (((16 + 4 * q + kk) ^ r16) << 4));
         }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -893,9 +896,11 @@ bool step_dma_supported(const StepArgs& a, int mode) {
   const int seg = h16 ? 8 : 4;   // elements of a 16-byte segment of R
   const uint64_t esize = h16 ? 2 : 4;
   if (a.H % seg != 0 || reinterpret_cast<uintptr_t>(a.R) % 16 != 0) return false;
-  // every offset, and the out-of-range marker above them, fits 32 bits
+  // every offset, and the out-of-range marker above them, fits 32 bits (mode
+  // 1: h as two f16 planes, an offset plus a plane)
   if (uint64_t(a.G) * a.H * a.H * esize >= kOutOfRange) return false;
   if (uint64_t(a.B) * a.H * 4 >= kOutOfRange) return false;
+  if (h16 && (uint64_t(a.D) + 1) * a.B * a.H * 2 >= kOutOfRange) return false;
   return true;
 }
 

@@ -26,8 +26,8 @@ struct StateLayout {
   size_t zbuf;     // f32 GRU z for the two-phase step: [D][B][H]
   size_t rhbuf;    // f32 GRU r*h for the two-phase step: [D][B][H]
   size_t rsplit;   // bf16 R as two planes (hi, lo) of [D][G*H][H] (f32 layers on the bf16 matrix cores)
-  size_t hsplit;   // bf16 h, two slots of two planes (hi, lo) of [D][B][H]
-  size_t rhsplit;  // bf16 GRU r*h, two planes of [D][B][H]
+  size_t hsplit;   // h as 16-bit halves (f16 or bf16): two slots of two planes (hi, lo) of [D][B][H]
+  size_t rhsplit;  // GRU r*h likewise: two planes of [D][B][H]
   size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
   size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
   size_t status;   // int: persistent engine status (1: a wait hit its safety bound)
@@ -58,6 +58,10 @@ struct Problem {
   bool f32_split_proj = false;
   // f32 tensors: the per-step matrix-core product on the bf16 matrix cores
   bool f32_split_step = false;
+  // the step that produces h also writes it as two 16-bit planes for the
+  // matrix-core step's operand: 1 f16 halves (f16 layers with the default
+  // activations), 2 bf16 halves (f32 layers on the bf16 matrix cores), 0 none
+  int h_split = 0;
 };
 
 // Arguments shared by the step kernels.
@@ -79,11 +83,13 @@ struct StepArgs {
   float* cell_state;       // [D][B][H]
   float* zbuf;             // [D][B][H]
   float* rhbuf;            // [D][B][H]
-  // f32 layers whose step product runs on the bf16 matrix cores (null
-  // otherwise): bf16 bit patterns, hi and lo planes of each tensor
-  unsigned short* rsplit;  // [2][D][G*H][H]
+  // 16-bit halves of R, h and r*h for the matrix-core step's operands (null
+  // when not used): bit patterns, hi and lo planes of each tensor.  R only for
+  // f32 layers on the bf16 matrix cores.
+  unsigned short* rsplit;  // [2][D][G*H][H], bf16
   unsigned short* hsplit;  // [2 slots][2][D][B][H]: slot s & 1 holds h of step s
   unsigned short* rhsplit; // [2][D][B][H]
+  int split_kind;          // of hsplit and rhsplit: 1 f16 halves, 2 bf16 halves
   unsigned long long* xch; // [2][D][B][H]
   unsigned long long* xch2;// [2][D][B][H]
   float clip;              // > 0: clamp
@@ -113,7 +119,8 @@ struct SetupArgs {
   const void* init_h;  // or null
   const void* init_c;  // or null
   float* hbuf;         // slot 0 of the per-step engine's h, or null (persistent engine)
-  unsigned short* hsplit;  // slot 0 of h as bf16 hi and lo planes, or null
+  unsigned short* hsplit;  // slot 0 of h as 16-bit hi and lo planes, or null
+  int split_kind;          // 1 f16 halves, 2 bf16 halves
   float* cell_state;   // or null (persistent engine)
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
