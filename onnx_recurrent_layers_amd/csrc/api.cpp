@@ -496,9 +496,12 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
       bool done = false;
       if (p.pers_mfma) {
         e = launch_step_mfma_persistent(a, p, flags, status, s);
-        if (e != hipSuccess && e != hipErrorNotSupported)
+        // not supported (R's alignment, epilogue planes) or not every tile
+        // resident at once on this device: one launch per step instead
+        if (e == hipErrorCooperativeLaunchTooLarge) (void)hipGetLastError();
+        if (e != hipSuccess && e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
           return fail(RNN_ERR_HIP, cell, "persistent matrix-core step launch: %s", hipGetErrorString(e));
-        done = e == hipSuccess;   // not supported (R's alignment, epilogue planes): one launch per step
+        done = e == hipSuccess;
       }
       for (int step = 0; !done && step < int(p.steps); ++step)
         if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
