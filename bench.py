@@ -64,7 +64,7 @@ class HipEvents:
 # the kernel sources still hash to what was profiled.
 TRAFFIC_PROFILES = {
     ("C2", "persistent"): os.path.join(ROOT, "profiles", "persistent_step_bilstm_s80_b1_h256_f32.md"),
-    ("C4", "launch"): os.path.join(ROOT, "profiles", "mfma_step_lstm_s256_b64_h1024_f16.md"),
+    ("C4", "persistent"): os.path.join(ROOT, "profiles", "persistent_mfma_step_lstm_s256_b64_h1024_f16.md"),
     ("C5", "launch"): os.path.join(ROOT, "profiles", "mfma_step_rnn_s1024_b256_h2048_f32.md"),
 }
 
