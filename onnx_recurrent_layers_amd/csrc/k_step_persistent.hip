@@ -602,8 +602,13 @@ bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per
   const int Gp = p.G - ((p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget) ? 1 : 0);
   const int NB = next_pow2_nb(int(p.B));
   const int maxw = 256 / p.D;  // one workgroup per compute unit
-  // about 64 R rows per workgroup (two per lane group); RNN_PERSISTENT_UNITS overrides for tuning
-  int U = std::max(1, 64 / Gp);
+  // R rows per workgroup: about 16 for the vector-ALU products (more
+  // workgroups share each step's products: C2 3.54 us per step at 16 rows
+  // against 3.73 at 32 and 3.76 at 64), about 64 for the matrix-core products
+  // (16-row blocks; C3 is 4 % slower at 24 rows than at 48 or 63).
+  // RNN_PERSISTENT_UNITS overrides the choice for tuning.
+  const bool mf_rows = p.esize == 2 && NB >= 4 && default_acts(p);
+  int U = std::max(1, (mf_rows ? 64 : 16) / Gp);
   if (const char* env = std::getenv("RNN_PERSISTENT_UNITS")) U = std::max(1, std::atoi(env));
   U = std::min(U, 64 / NB);
   int wpd = int((p.H + U - 1) / U);
@@ -613,8 +618,7 @@ bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per
     wpd = int((p.H + U - 1) / U);
   }
   if (U * NB > 64) return false;  // one gate thread per (unit, batch row), all in wave 0
-  const bool mf = p.esize == 2 && NB >= 4 && default_acts(p);
-  if (lds_bytes(Gp * U, int(p.H), p.esize, NB, mf) > kLdsLimit) return false;
+  if (lds_bytes(Gp * U, int(p.H), p.esize, NB, mf_rows) > kLdsLimit) return false;
   *blocks = wpd * p.D;
   *units = U;
   *wg_per_dir = wpd;
