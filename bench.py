@@ -128,6 +128,9 @@ def main() -> int:
     ap.add_argument("--engine", default="auto", choices=["auto", "launch", "persistent"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-floors", action="store_true",
+                    help="skip the step-floor layers (for profiler runs, whose kernel statistics then cover the "
+                         "workload alone)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device copy of this many bytes (a known-size "
                          "kernel against which the HBM byte counters of a profiler are scaled)")
@@ -238,6 +241,33 @@ def main() -> int:
         "projection": {"tflops": round(proj_tflops, 3), "peak_tflops": MFMA_PEAK_TFLOPS[spec.dtype],
                        "frac": round(proj_tflops / MFMA_PEAK_TFLOPS[spec.dtype], 5)},
     }
+
+    # floors of a step on this device, measured with the library itself on a
+    # layer too small to have any arithmetic to speak of (the workload's
+    # cell, seq, one batch row, input and hidden 8): one launch per step, and
+    # the persistent engine's exchange between workgroups
+    floors = {}
+    for eng in (() if args.no_floors else ("launch", "persistent")):
+        fspec = spec.replace(batch=1, input=8, hidden=8, lens=False, max_length=0, layout=0,
+                             direction=spec.direction)
+        finp = synth.make_inputs(fspec, 1)
+        ften = rl.to_device(finp, "cuda:0")
+        fouts = {n: torch.empty(rl.output_shapes(fspec)[n], dtype=dt, device=dev) for n in fspec.outputs
+                 if not (n == "Y_c" and fspec.cell != "LSTM")}
+        flayer = rl.Layer(fspec, engine=eng, device="cuda:0")
+        fall = {**ften, **fouts}
+        for _ in range(3):
+            flayer.encode(fall)
+        fev = HipEvents(5 * 10)
+        for i in range(10):
+            flayer.encode(fall, events=fev.ev[5 * i:5 * i + 5])
+        torch.cuda.synchronize()
+        fsteps = statistics.median([fev.ms(5 * i + 2, 5 * i + 3) for i in range(10)])
+        fev.close()
+        floors[eng + "_per_step_us"] = round(fsteps * 1000.0 / max(1, flayer.plan.steps), 3)
+        del flayer
+    if floors:
+        line["step_floor"] = {**floors, "layer": f"{spec.cell} seq {spec.seq}, batch 1, input 8, hidden 8"}
 
     if not args.no_cpu_baseline:
         # the oracle on a bounded sample: whole layers while one takes under
