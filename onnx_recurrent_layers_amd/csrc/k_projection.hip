@@ -14,6 +14,7 @@
 // so that Xw is written time-major ([D][S][B][G*H], row t*B+b).  Tiles that
 // fall entirely in a gate block nobody reads (input_forget's f) are skipped.
 #include <algorithm>
+#include <cstdlib>
 
 #include "device_common.h"
 
@@ -335,6 +336,150 @@ __global__ __launch_bounds__(256) void projection_bf16x3_kernel(ProjArgs a, Setu
       }
 }
 
+// Small projections (fewer than 256 tiles of 64x64: C2's 80 x 1024 x 256 per
+// direction, say) are latency-bound: the tiled kernel above walks K in eight
+// or more chunks, one memory round trip each, on a quarter of the compute
+// units.  Here a workgroup owns a 32x32 output tile, which gives 3 to 4 times
+// as many workgroups, and its four waves split K: the K axis is cut into
+// blocks of 2*NSEG segments of 16 bytes, wave w takes blocks w, w+4, ...
+// Inside a block lane l reads NSEG consecutive segments of row l%32 of X (A
+// operand) and of W (B operand) straight into registers, lanes 0-31 the first
+// half of the block and lanes 32-63 the second; MFMA step j then pairs the two
+// halves' j-th k values (32x32x2 f32) or 8-value runs (32x32x16 f16).  A and
+// B use the same k assignment, so every product is a genuine X*W term, and
+// the order is fixed.  No LDS staging: a block is one round of loads.  The
+// four waves' partial tiles are added in wave order through LDS.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void projection_small_kernel(ProjArgs a, SetupArgs sa, int gemm_blocks) {
+  constexpr int SEG = ProjCfg<T>::SEG, NSEG = 8;
+  constexpr int HALF = NSEG * SEG;  // k of one half-wave in a block
+  constexpr int KBLK = 2 * HALF;    // k of one block
+  typedef typename Seg<T>::type V;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+  __shared__ float red[4][32][33];
+
+  if (int(blockIdx.x) >= gemm_blocks) {
+    setup_state<T>(sa, int(blockIdx.x) - gemm_blocks, int(gridDim.x) - gemm_blocks);
+    return;
+  }
+  const int64_t mt = (a.M + 31) / 32, nt = (a.N + 31) / 32;
+  const int64_t lin = blockIdx.x;
+  const int64_t mi = lin % mt, ni = (lin / mt) % nt;
+  const int d = int(lin / (mt * nt));
+  const int64_t m0 = mi * 32, n0 = ni * 32;
+  if (a.skip_block >= 0 && n0 >= a.skip_block * a.H && n0 + 32 <= (a.skip_block + 1) * a.H) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, half = lane >> 5;
+  const T* X = static_cast<const T*>(a.X);
+  const T* W = static_cast<const T*>(a.W) + int64_t(d) * a.N * a.K;
+  // Loads are unconditional, from clamped addresses (a load under a lane
+  // condition makes the compiler wait for it before issuing the next one), and
+  // the values are masked where they are used.  Only k past K needs masking,
+  // in both operands, so that such a product is exactly zero; a row past M or
+  // N feeds only outputs that are dropped.  The mask is a bit mask, not a
+  // select, which keeps the compiler from moving the loads into branches.
+  const T* ap = X + x_row(m0 + r32 < a.M ? m0 + r32 : a.M - 1, a.S, a.B, a.layout) * a.K;
+  const T* bp = W + (n0 + r32 < a.N ? n0 + r32 : a.N - 1) * a.K;
+  auto seg = [&](const T* p, int64_t k) {
+    if constexpr (VEC) {  // K is a whole number of segments
+      return *reinterpret_cast<const u32x4*>(p + (k < a.K ? k : 0));
+    } else if constexpr (sizeof(T) == 4) {
+      u32x4 u;
+#pragma unroll
+      for (int z = 0; z < SEG; ++z) u[z] = reinterpret_cast<const unsigned*>(p)[k + z < a.K ? k + z : a.K - 1];
+      return u;
+    } else {
+      u16x8 u;
+#pragma unroll
+      for (int z = 0; z < SEG; ++z) u[z] = reinterpret_cast<const unsigned short*>(p)[k + z < a.K ? k + z : a.K - 1];
+      return __builtin_bit_cast(u32x4, u);
+    }
+  };
+  // mask of the 32-bit words of the segment at k: all ones where k is inside K
+  auto kmask = [&](int64_t k) {
+    u32x4 m;
+    if constexpr (VEC) {
+      m = u32x4(0u - unsigned(k < a.K));
+    } else if constexpr (sizeof(T) == 4) {
+#pragma unroll
+      for (int z = 0; z < 4; ++z) m[z] = 0u - unsigned(k + z < a.K);
+    } else {
+#pragma unroll
+      for (int z = 0; z < 4; ++z)
+        m[z] = ((0u - unsigned(k + 2 * z < a.K)) & 0xffffu) | ((0u - unsigned(k + 2 * z + 1 < a.K)) & 0xffff0000u);
+    }
+    return m;
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // One round of loads per block.  For K up to 256 f32 or 512 f16 values
+  // every wave has at most one block, so the tile takes one memory round
+  // trip.  (Prefetching the next block into a second register set was undone
+  // by the compiler, which moved those loads past the loop's exit test to
+  // where they are used.)
+  const int64_t nblk = (a.K + KBLK - 1) / KBLK;
+  for (int64_t blk = wave; blk < nblk; blk += 4) {
+    const int64_t k0 = blk * KBLK + half * HALF;
+    u32x4 ra[NSEG], rb[NSEG];
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      ra[i] = seg(ap, k0 + i * SEG);
+      rb[i] = seg(bp, k0 + i * SEG);
+    }
+    // keep the scheduler from moving each load down to its use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      const u32x4 m = kmask(k0 + i * SEG);
+      const V va = __builtin_bit_cast(V, ra[i] & m), vb = __builtin_bit_cast(V, rb[i] & m);
+      if constexpr (sizeof(T) == 2) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, vb, acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], vb[e], acc, 0, 0, 0);
+      }
+    }
+  }
+
+  // 32x32 accumulator layout: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * half + (r & 3)][r32] = acc[r];
+  __syncthreads();
+  const int nw = int(nblk < 4 ? nblk : 4);  // waves that own a block
+  float* out = a.xw + int64_t(d) * a.M * a.N;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, row = e >> 5, col = e & 31;
+    const int64_t m = m0 + row, n = n0 + col;
+    if (m < a.M && n < a.N) {
+      float v = red[0][row][col];
+      for (int w = 1; w < nw; ++w) v += red[w][row][col];
+      out[m * a.N + n] = v;
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_small(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s) {
+  const int64_t mt = (a.M + 31) / 32, nt = (a.N + 31) / 32;
+  const int64_t gemm = (a.M > 0 && a.N > 0) ? mt * nt * a.D : 0;
+  if (gemm + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int seg = ProjCfg<T>::SEG;
+  const bool vec = a.K % seg == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+  const dim3 grid(unsigned(gemm + setup_blocks));
+  if (vec)
+    hipLaunchKernelGGL((projection_small_kernel<T, true>), grid, dim3(256), 0, s, a, sa, int(gemm));
+  else
+    hipLaunchKernelGGL((projection_small_kernel<T, false>), grid, dim3(256), 0, s, a, sa, int(gemm));
+  return hipGetLastError();
+}
+
 template <int BM, int BN>
 static hipError_t launch_bf16x3(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s) {
   const int64_t mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
@@ -376,9 +521,16 @@ hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, 
     const hipError_t e = launch_projection_lds(a, sa, setup_blocks, s);
     if (e != hipErrorNotSupported) return e;
   }
-  // 128x128 tiles when they still give every compute unit a workgroup, else 64x64
+  // 128x128 tiles when they still give every compute unit a workgroup, else
+  // 64x64; below 256 tiles of 64x64 the latency-bound small kernel
   const int64_t big = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.D;
   const bool use_big = big >= 256;
+  const int64_t mid = ((a.M + 63) / 64) * ((a.N + 63) / 64) * a.D;
+  bool small = mid < 256;
+  if (const char* e = std::getenv("RNN_SMALL_PROJECTION")) small = std::atoi(e) != 0;  // forces it on (1) or off (0)
+  if (small && !(dtype == RNN_DTYPE_F32 && a.f32_split))
+    return dtype == RNN_DTYPE_F32 ? launch_small<float>(a, sa, setup_blocks, s)
+                                  : launch_small<half_t>(a, sa, setup_blocks, s);
   if (dtype == RNN_DTYPE_F32) {
     if (a.f32_split)
       return use_big ? launch_bf16x3<128, 128>(a, sa, setup_blocks, s) : launch_bf16x3<64, 64>(a, sa, setup_blocks, s);

@@ -56,6 +56,48 @@ def test_projection_scratch(dtype, layout):
         assert err <= 1e-4, (d, err)
 
 
+# The latency-bound projection kernel for small layers (32x32 tiles, K split
+# over the four waves, one round of loads per K block), forced on (and, for
+# comparison, off) with RNN_SMALL_PROJECTION: whole K blocks and ragged ones,
+# K not a whole number of 16-byte segments (element loads), several blocks
+# per wave, tiles inside the skipped f block, M and N below one tile.
+@pytest.mark.parametrize("dtype,layout,cell,input_forget,S,B,I,H", [
+    ("f32", 0, "LSTM", 0, 13, 11, 70, 37),
+    ("f32", 1, "GRU", 0, 9, 5, 256, 64),
+    ("f16", 0, "RNN", 0, 7, 3, 520, 40),
+    ("f32", 0, "LSTM", 1, 5, 2, 1000, 64),
+    ("f16", 1, "LSTM", 1, 6, 4, 77, 50),
+    ("f32", 0, "LSTM", 0, 8, 1, 16, 32),
+])
+@pytest.mark.parametrize("force", ["1", "0"])
+def test_projection_small_kernel(dtype, layout, cell, input_forget, S, B, I, H, force, monkeypatch):
+    import torch
+    monkeypatch.setenv("RNN_SMALL_PROJECTION", force)
+    spec = LayerSpec(cell, seq=S, batch=B, input=I, hidden=H, layout=layout, dtype=dtype, input_forget=input_forget,
+                     direction="bidirectional", outputs=("Y_h",))
+    inp = make_inputs(spec, 9)
+    note(f"case projection small={force} {dtype} {cell} L{layout} S{S} B{B} I{I} H{H}")
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    D, G = 2, spec.gates
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
+    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
+    A = X.reshape(S * B, I)
+    for d in range(D):
+        ref = oracle.projection(A, inp["W"][d])
+        cols = np.ones(G * H, bool)
+        if input_forget:
+            cols[2 * H:3 * H] = False     # the f block is not computed
+        # f16 products are exact in f32 and f32 products round once; the f32
+        # sums of K terms (in any fixed order) stay within (K + 4) * 2^-23 of
+        # sum |x_k * w_k|
+        bound = (I + 4) * 2.0 ** -23 * (np.abs(A.astype(np.float64)) @ np.abs(inp["W"][d].astype(np.float64)).T)
+        err = np.abs(xw[d][:, cols].astype(np.float64) - ref[:, cols])
+        assert np.all(err <= bound[:, cols] + 1e-30), (d, float(np.max(err / (bound[:, cols] + 1e-30))))
+    # and the whole layer through it
+    check(spec, inp, engine="launch", twice=False, what=f"small projection {force}")
+
+
 # f32 tensors with the projection on the bf16 matrix cores (three split
 # products, forced with RNN_F32_SPLIT=1 on small shapes).  Each element of Xw
 # must lie within 2^-15 * sum_k |x_k * w_k| of the exact product: the split
