@@ -73,7 +73,7 @@ typedef struct {
 typedef enum {
   RNN_ENGINE_AUTO = 0,
   RNN_ENGINE_LAUNCH = 1,      /* one kernel launch per step (two for GRU linear_before_reset=0) */
-  RNN_ENGINE_PERSISTENT = 2   /* one cooperative launch for all steps (small batches) */
+  RNN_ENGINE_PERSISTENT = 2   /* one launch for all steps (small batches; the matrix-core step for batches of 16 and more) */
 } rnn_engine;
 
 /* Layer description (the page's RecurrentProblem plus ONNX attributes). */
@@ -134,8 +134,8 @@ void rnn_problem_destroy(rnn_problem* problem);
  *                  time-major [D][S][B][G*H] (row t*B+b of direction d holds
  *                  X[t,b,:] . W[d]^T);
  *   *state_bytes = the f32 hidden state (two slots of [D][B][H]), the f32
- *                  cell state, the GRU two-pass buffers, or the persistent
- *                  engine's exchange words.
+ *                  cell state, the GRU two-pass buffers, and for the
+ *                  persistent engine its exchange words and status words.
  * Either may be 0 (then the matching pointer may be NULL).  Both buffers must
  * be 256-byte aligned; they may be two regions of one arena. */
 int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state_bytes);

@@ -221,7 +221,13 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     p->pers_wg_per_dir = wpd;
     st.xch = off;   off = align256(off + 2 * size_t(dbh) * 8);
     st.xch2 = off;  off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
-    st.status = off; off = align256(off + 4);
+    st.status = off; off = align256(off + 3 * 4);   // status, arrival tickets, residency decision
+    // the per-step engine's state, for the fallback taken when the grid does
+    // not run all at once
+    st.hbuf = off;  off = align256(off + 2 * size_t(dbh) * 4);
+    st.cell = off;  off = align256(off + size_t(dbh) * 4);
+    st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+    st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
   } else {
     st.hbuf = off;  off = align256(off + 2 * size_t(dbh) * 4);
     st.cell = off;  off = align256(off + size_t(dbh) * 4);
@@ -378,8 +384,8 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* st = static_cast<char*>(state_scratch);
   const bool pers = p.engine == RNN_ENGINE_PERSISTENT && !p.pers_mfma;   // the small-batch persistent engine
-  float* hbuf = pers ? nullptr : reinterpret_cast<float*>(st + p.st.hbuf);
-  float* cstate = pers ? nullptr : reinterpret_cast<float*>(st + p.st.cell);
+  float* hbuf = reinterpret_cast<float*>(st + p.st.hbuf);
+  float* cstate = reinterpret_cast<float*>(st + p.st.cell);
   int* status = (pers || p.pers_mfma) ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
   int* flags = p.pers_mfma ? reinterpret_cast<int*>(st + p.st.flags) : nullptr;
 
@@ -404,14 +410,12 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   sa.status = status;
   sa.flags = flags;
   sa.nflags = flags ? kPersistentMfmaTiles : 0;
-  if (!pers) {
-    sa.Y = const_cast<char*>(Y);
-    sa.Y_h = const_cast<char*>(Yh);
-    sa.Y_c = const_cast<char*>(Yc);
-    sa.lens = reinterpret_cast<const int32_t*>(lens);
-    sa.S = int(p.S);
-    sa.steps = int(p.steps);
-  }
+  sa.Y = const_cast<char*>(Y);
+  sa.Y_h = const_cast<char*>(Yh);
+  sa.Y_c = const_cast<char*>(Yc);
+  sa.lens = reinterpret_cast<const int32_t*>(lens);
+  sa.S = int(p.S);
+  sa.steps = int(p.steps);
 
   StepArgs a{};
   a.cell = cell;

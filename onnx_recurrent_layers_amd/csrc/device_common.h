@@ -157,7 +157,8 @@ __device__ __forceinline__ void setup_state(const SetupArgs& a, int part, int pa
       }
     }
   }
-  if (a.status && part == 0 && threadIdx.x == 0) *a.status = 0;
+  // status word, arrival tickets and residency decision of a persistent launch
+  if (a.status && part == 0 && threadIdx.x < 3) a.status[threadIdx.x] = 0;
   for (int i = part * int(blockDim.x) + int(threadIdx.x); i < a.nflags; i += parts * int(blockDim.x)) a.flags[i] = 0;
 }
 

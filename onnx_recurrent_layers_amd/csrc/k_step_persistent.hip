@@ -1,14 +1,26 @@
 // k_step_persistent.hip -- stage 3 of a layer ("Recurrent layers" page, "How a
-// layer runs", item 3) for small batches as ONE cooperative launch that walks
-// every step, followed directly by the page's output rules ("Semantics").
+// layer runs", item 3) for small batches as ONE launch that walks every step,
+// followed directly by the page's output rules ("Semantics").
 //
 // Why not a pass per step: the page avoids a grid-wide dependency because its
-// APIs cannot guarantee co-resident workgroups ("Why a pass per step").  HIP's
-// cooperative launch does guarantee it, so here each workgroup keeps its share
-// of R resident in LDS for the whole layer and the steps are ordered by
-// per-value handshakes instead of kernel boundaries.  The page's own
-// one-workgroup-per-direction attempt lost because every step's R went
-// through one compute unit; here R is spread over up to 256 compute units.
+// APIs cannot guarantee co-resident workgroups ("Why a pass per step").  Here
+// each workgroup keeps its share of R resident in LDS for the whole layer and
+// the steps are ordered by per-value handshakes instead of kernel boundaries.
+// The page's own one-workgroup-per-direction attempt lost because every step's
+// R went through one compute unit; here R is spread over up to 256 compute
+// units.
+//
+// Residency: HIP's cooperative launch guarantees co-resident workgroups, but
+// on this runtime it costs about 18 us per launch (a sixteenth of a 80-step
+// layer).  So the grid is launched plainly (after a host check that it fits
+// the device) and the workgroups first agree whether all of them are running:
+// each takes an arrival ticket; the first to see every ticket taken records
+// GO, and one that waits past a short window records ABORT with the number of
+// tickets taken by then (one compare-and-swap decides).  On GO the fast path
+// below runs.  On ABORT (the device was partly held by other work) the
+// workgroups that had arrived run the layer one direction per workgroup,
+// which needs no other workgroup: slower, but correct, and never a wait on a
+// workgroup that may not be scheduled.
 //
 // Exchange: the hidden state of step s travels as 64-bit words
 // (tag = step << 32 | f32 bits) stored and loaded with agent-scope relaxed
@@ -25,7 +37,7 @@
 #include <algorithm>
 #include <cstdlib>
 
-#include "cells.h"
+#include "step_wave.h"
 
 namespace rnnhip {
 
@@ -47,7 +59,8 @@ struct PersArgs {
   void* Y;
   void* Y_h;
   void* Y_c;
-  int* status;      // set to 1 if a wait ran past the safety bound
+  int* status;      // [0] set to 1 if a wait ran past the safety bound; [1] arrival tickets, [2] residency decision
+  int fallback;     // > 0: take the fallback with this many workgroups (tests); 0: decide by arrival
 };
 
 __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
@@ -147,6 +160,62 @@ __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, cons
   for (int i = 0; i < kChunk; ++i)
     if (w.want[i]) store_h<MF>(hs, m.off[i], lo, __uint_as_float(static_cast<unsigned>(w.v[i])));
   return fail;
+}
+
+// Residency decision, taken by thread 0 of every workgroup.  coop[0] counts
+// arrivals, coop[1] holds the decision: 1 (GO: every workgroup is running)
+// or 2 | count << 8 (ABORT: the workgroups with tickets below count run the
+// fallback).  Both are zeroed by the state setup that precedes the kernel on
+// the stream.  `forced` > 0 makes the first arrival record ABORT with that
+// count at once (tests of the fallback).
+constexpr unsigned long long kArrivalWindow = 5000;  // ticks of the 100 MHz real-time counter: 50 us
+
+// Split in two so that the workgroup loads its rows of R between taking its
+// ticket and waiting for the decision: the last workgroup to arrive records
+// GO itself, and the others see it about when their rows have landed.
+__device__ __forceinline__ int arrive_ticket(int* coop) {
+  return __hip_atomic_fetch_add(&coop[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ int arrive_decide(int* coop, int n_groups, int forced, int ticket) {
+  int want = 0;
+  if (forced > 0) {
+    if (ticket == 0) want = 2 | (min(forced, n_groups) << 8);
+  } else if (ticket == n_groups - 1) {
+    want = 1;
+  }
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    if (want != 0) {
+      int expect = 0;
+      __hip_atomic_compare_exchange_strong(&coop[1], &expect, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      want = 0;
+    }
+    const int dec = __hip_atomic_load(&coop[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dec != 0) return dec;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kArrivalWindow)
+      want = 2 | (__hip_atomic_load(&coop[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 8);
+    else
+      __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The whole layer for direction d by one workgroup alone: its waves walk the
+// units of each step with the per-step engine's wave body on the per-step
+// engine's state (h slots, cell state, GRU z and r*h, all set up by the state
+// setup), with a workgroup barrier between steps and between the two phases
+// of a GRU step with linear_before_reset = 0.
+template <typename T>
+__device__ __forceinline__ void fallback_direction(const StepArgs& a, int d) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tasks = a.H * ((a.B + kRows - 1) / kRows);
+  const int phases = (a.cell == RNN_CELL_GRU && !a.lbr) ? 2 : 1;
+  for (int s = 0; s < a.steps; ++s)
+    for (int ph = 0; ph < phases; ++ph) {
+      for (int t = wave; t < tasks; t += kPThreads / 64) step_wave<T>(a, s, ph, t % a.H, (t / a.H) * kRows, d, lane);
+      __syncthreads();
+    }
 }
 
 // Whole stage, run by the polling waves only (ptid = thread index among
@@ -341,6 +410,10 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   constexpr bool MF = mfma_products<T, NB, DEF>();
   const int HS = H4 + 8;             // row stride of the f16 planes of h
 
+  // arrival ticket now, the residency decision after the R rows are loaded
+  int ticket = 0;
+  if (tid == 0) ticket = arrive_ticket(p.status + 1);
+
   // LDS: R rows | copy of h | recurrent sums (f32 [NR][NB], or the four
   // partials [4][NR][NB] of the matrix-core products)
   T* Rl = reinterpret_cast<T*>(smem);
@@ -368,6 +441,20 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     for (int e = tid; e < 2 * NB * HS; e += kPThreads) static_cast<half_t*>(hs)[e] = half_t(0.f);
   } else {
     for (int e = NB * H + tid; e < NB * H4; e += kPThreads) static_cast<float*>(hs)[e] = 0.f;
+  }
+
+  // every workgroup running, or the fallback
+  __shared__ int coop_dec, coop_ticket;
+  if (tid == 0) {
+    coop_dec = arrive_decide(p.status + 1, int(gridDim.x), p.fallback, ticket);
+    coop_ticket = ticket;
+  }
+  __syncthreads();
+  if (coop_dec != 1) {
+    const int cnt = coop_dec >> 8;
+    if (coop_ticket < cnt)
+      for (int dd = coop_ticket; dd < a.D; dd += cnt) fallback_direction<T>(a, dd);
+    return;
   }
 
   int maxL = 0;
@@ -406,17 +493,8 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
       peep[1] = ld(P, H + j);
       peep[2] = ld(P, 2 * H + j);
     }
-    // outputs that no step writes: Y past the length, final states of an empty row
-    if (p.Y)
-      for (int t = L; t < S; ++t) {
-        const int64_t yi = p.layout == 0 ? ((int64_t(t) * a.D + d) * B + g_b) * H + j
-                                         : ((int64_t(g_b) * S + t) * a.D + d) * H + j;
-        static_cast<T*>(p.Y)[yi] = to_elem<T>(0.f);
-      }
-    if (L == 0) {
-      if (p.Y_h) static_cast<T*>(p.Y_h)[sidx] = to_elem<T>(0.f);
-      if (p.Y_c) static_cast<T*>(p.Y_c)[sidx] = to_elem<T>(0.f);
-    }
+    // (the outputs no step writes, Y past the length and the final states of
+    // an empty row, are written by the state setup)
   }
   __shared__ int abort_flag;
   if (tid == 0) abort_flag = 0;
@@ -632,16 +710,12 @@ static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStrea
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
   PersArgs arg = pa;
-  // RNN_PLAIN_LAUNCH=1 launches the same kernel and grid without the
-  // cooperative API, after checking on the host that every workgroup fits on
-  // the chip at once.  It exists for profilers that fail on cooperative
-  // launches; the default is the cooperative launch, which guarantees that
-  // all workgroups are resident together.
-  static const bool plain = [] {
-    const char* e = std::getenv("RNN_PLAIN_LAUNCH");
-    return e && e[0] == '1';
-  }();
-  if (plain) {
+  // A plain launch after checking on the host that every workgroup fits on
+  // the device at once; the kernel itself settles whether they all run
+  // together (see the top of this file).  RNN_COOPERATIVE_LAUNCH=1 takes the
+  // cooperative launch instead (about 18 us more per launch here).
+  const char* coop_env = std::getenv("RNN_COOPERATIVE_LAUNCH");
+  if (!(coop_env && coop_env[0] == '1')) {
     int per_cu = 0, dev = 0, cus = 0;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kPThreads,
                                                            lds)) != hipSuccess)
@@ -678,6 +752,7 @@ hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const Per
   pa.Y_h = io.Y_h;
   pa.Y_c = io.Y_c;
   pa.status = io.status;
+  if (const char* e = std::getenv("RNN_PERSISTENT_FALLBACK")) pa.fallback = std::max(0, std::atoi(e));
   const int NB = next_pow2_nb(a.B);
   const int blocks = p.pers_blocks;
   const bool def = default_acts(p);

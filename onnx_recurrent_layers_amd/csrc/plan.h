@@ -30,7 +30,7 @@ struct StateLayout {
   size_t rhsplit;  // GRU r*h likewise: two planes of [D][B][H]
   size_t xch;      // u64 tagged exchange words of the persistent engine: [2][D][B][H]
   size_t xch2;     // u64 tagged r*h words (GRU, linear_before_reset = 0): [2][D][B][H]
-  size_t status;   // int: persistent engine status (1: a wait hit its safety bound)
+  size_t status;   // int[3]: persistent engine status (1: a wait hit its safety bound), arrival tickets, residency decision
   size_t flags;    // int per workgroup of the persistent matrix-core step: phases finished
   size_t total;
 };
@@ -118,18 +118,17 @@ struct SetupArgs {
   int dtype;
   const void* init_h;  // or null
   const void* init_c;  // or null
-  float* hbuf;         // slot 0 of the per-step engine's h, or null (persistent engine)
+  float* hbuf;         // slot 0 of the per-step engine's h (also the persistent engine's fallback), or null
   unsigned short* hsplit;  // slot 0 of h as 16-bit hi and lo planes, or null
   int split_kind;          // 1 f16 halves, 2 bf16 halves
   float* cell_state;   // or null (persistent engine)
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
-  int* status;               // persistent engine status word, or null
+  int* status;               // persistent engine status word and the two residency words after it, or null
   int* flags;                // workgroup flags of the persistent matrix-core step, zeroed here, or null
   int nflags;
-  // outputs no step of the per-step engine writes (null for the persistent
-  // engine, which writes them itself): Y past each row's length, the final
-  // states of rows of length 0, and every final state when Seq = 0
+  // outputs no step writes: Y past each row's length, the final states of
+  // rows of length 0, and every final state when Seq = 0
   void* Y;
   void* Y_h;
   void* Y_c;

@@ -223,6 +223,58 @@ def test_persistent_matrix_products(cell, direction, layout, opt, B, H):
     check(spec, inp, engine="persistent", what=f"persistent mfma {cell}/{direction}/L{layout}/{opt}/B{B}/H{H}")
 
 
+def _residency_words(layer, spec):
+    """status, arrival tickets and residency decision of the small-batch
+    persistent engine, read back from the state scratch (they follow the two
+    slots of exchange words, and the r*h words of a GRU with
+    linear_before_reset = 0)."""
+    import torch
+    al = lambda n: (n + 255) // 256 * 256
+    dbh = (2 if spec.direction == "bidirectional" else 1) * spec.batch * spec.hidden
+    off = al(16 * dbh)
+    if spec.cell == "GRU" and not spec.linear_before_reset:
+        off += al(16 * dbh)
+    torch.cuda.synchronize()
+    return [int(v) for v in layer.state[off:off + 12].view(torch.int32).cpu()]
+
+
+# The persistent engine is launched plainly and its workgroups agree first
+# whether all of them run at once (GO), else the ones that arrived run the
+# layer one direction per workgroup (the fallback).  The fallback is forced
+# here with RNN_PERSISTENT_FALLBACK = k (k workgroups take part): every cell
+# and GRU form, lengths with 0, initial states, peepholes, clip,
+# input_forget, both dtypes (the vector-ALU and the matrix-core instances),
+# both layouts; then the residency words show which path ran.
+FALLBACK = [("LSTM", 0, "f32", 0), ("LSTM", 1, "f16", 1), ("GRU", 0, "f32", 1), ("GRU", 1, "f16", 0),
+            ("RNN", 0, "f32", 0), ("LSTM", 0, "f16", 0)]
+
+
+@pytest.mark.parametrize("cell,opt,dtype,layout", FALLBACK, ids=[f"{c}-{o}-{d}-L{l}" for c, o, d, l in FALLBACK])
+@pytest.mark.parametrize("forced", ["1", "2"])
+def test_persistent_fallback(cell, opt, dtype, layout, forced, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    monkeypatch.setenv("RNN_PERSISTENT_FALLBACK", forced)
+    B = 5 if dtype == "f32" else 6
+    spec = LayerSpec(cell, seq=10, batch=B, input=37, hidden=70, direction="bidirectional", layout=layout,
+                     dtype=dtype, linear_before_reset=opt if cell == "GRU" else 0,
+                     input_forget=opt if cell == "LSTM" else 0, peephole=cell == "LSTM", clip=2.5,
+                     init_h=True, init_c=cell == "LSTM", lens=True, outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 61, Dists(sequence_lens=("I", 0, 10)))
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_blocks > 2
+    note(f"case persistent fallback {forced} {cell}/opt{opt}/{dtype}/L{layout}")
+    got = gpu_layer(spec, inp, layer=layer)
+    compare(spec, got, oracle.run(spec, inp, outputs=spec.outputs), what=f"fallback {forced} {cell}")
+    status, arrivals, decision = _residency_words(layer, spec)
+    assert status == 0 and decision == (2 | (int(forced) << 8)), (status, arrivals, decision)
+    # and without the switch, the fast path
+    monkeypatch.delenv("RNN_PERSISTENT_FALLBACK")
+    again = gpu_layer(spec, inp, layer=layer)
+    compare(spec, again, oracle.run(spec, inp, outputs=spec.outputs), what=f"persistent {cell}")
+    status, arrivals, decision = _residency_words(layer, spec)
+    assert status == 0 and decision == 1 and arrivals == layer.plan.step_blocks, (status, arrivals, decision)
+
+
 LARGE = [(c, d, dt) for c in ("LSTM", "GRU", "RNN") for d in ("forward", "bidirectional") for dt in ("f32", "f16")]
 
 
