@@ -168,7 +168,11 @@ __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, cons
 // fallback).  Both are zeroed by the state setup that precedes the kernel on
 // the stream.  `forced` > 0 makes the first arrival record ABORT with that
 // count at once (tests of the fallback).
-constexpr unsigned long long kArrivalWindow = 5000;  // ticks of the 100 MHz real-time counter: 50 us
+// A workgroup waits this long for the others before it records ABORT: a
+// healthy grid arrives within a few microseconds, but the first launch in a
+// process has been seen to take longer, and a needless fallback costs far
+// more than the wait.
+constexpr unsigned long long kArrivalWindow = 100000;  // ticks of the 100 MHz real-time counter: 1 ms
 
 // Split in two so that the workgroup loads its rows of R between taking its
 // ticket and waiting for the decision: the last workgroup to arrive records

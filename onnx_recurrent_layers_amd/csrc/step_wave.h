@@ -112,18 +112,21 @@ __device__ __forceinline__ void step_wave(const StepArgs& a, int s, int phase, i
     p4[1] = pre(1);
     p4[2] = a.input_forget ? 0.f : pre(2);
     p4[3] = pre(3);
-    float peep[3];
-    const float* pp = nullptr;
+    // (two calls, each with a fixed peephole pointer, so that the array stays
+    // in registers instead of scratch memory)
+    float peep[3] = {0.f, 0.f, 0.f};
     if (a.P) {
       const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
       peep[0] = ld(P, j);
       peep[1] = ld(P, H + j);
       peep[2] = ld(P, 2 * H + j);
-      pp = peep;
     }
     float* cst = a.cell_state + dBH + sidx;
     float h, c;
-    lstm_unit(p4, pp, *cst, a.clip, a.input_forget, acts, &h, &c);
+    if (a.P)
+      lstm_unit(p4, peep, *cst, a.clip, a.input_forget, acts, &h, &c);
+    else
+      lstm_unit(p4, nullptr, *cst, a.clip, a.input_forget, acts, &h, &c);
     *cst = c;
     hnext[sidx] = h;
     store_outputs<T>(a, d, b, j, t, s == Lr - 1, h, c);
