@@ -47,6 +47,9 @@ typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond every resource size used here
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kLdsBudget = 144 * 1024;          // staging bytes per workgroup
+// R resident in LDS (persistent form, f16 mode): the tile's R rows for every
+// k chunk, loaded once per layer; the chunk slots then carry h alone.
+constexpr int kRresBytes = 104 * 1024;
 
 // s_waitcnt immediate of the gfx9 encoding: vector-memory count vm (6 bits,
 // split), export count left open, LDS count lgkm.
@@ -83,17 +86,18 @@ template <> struct DmaGeo<2> {           // bf16 hi/lo planes of h and R (f32 te
   static constexpr int BELEMS = 8;
 };
 
-template <int MODE, int BM, int CB>
+template <int MODE, int BM, int CB, bool RR = false>
 struct DmaCfg {
   typedef DmaGeo<MODE> Geo;
   static constexpr int A_BYTES = BM * Geo::ASEGS * 16;
-  static constexpr int B_BYTES = CB * 4 * 16 * 256;           // 16 rows x 16 segments per column block
+  static constexpr int B_BYTES = RR ? 0 : CB * 4 * 16 * 256;    // 16 rows x 16 segments per column block
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int REC = BM * (kMaxNC + 1) * 4;             // product tile, over slot 0
-  static constexpr int NS0 = (kLdsBudget - (REC > STAGE ? REC - STAGE : 0)) / STAGE;
+  static constexpr int BUDGET = kLdsBudget - (RR ? kRresBytes : 0);
+  static constexpr int NS0 = (BUDGET - (REC > STAGE ? REC - STAGE : 0)) / STAGE;
   static constexpr int NS = NS0 > 4 ? 4 : NS0;                  // chunks resident (NS - 1 in flight)
   static constexpr int LA = A_BYTES / 1024 / 4;                 // h loads per wave per chunk
-  static constexpr int LB = 4 * CB;                             // R loads per wave per chunk
+  static constexpr int LB = RR ? 0 : 4 * CB;                    // R loads per wave per chunk
   static constexpr int L = LA + LB;
   static_assert(NS >= 2, "two chunks must fit in LDS");
   static_assert((A_BYTES / 1024) % 4 == 0, "h loads must split evenly over the four waves");
@@ -440,10 +444,13 @@ __device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& fi
 }
 
 // One step (one phase of a two-phase GRU step) of one tile, run by a
-// per-step launch (PERS = false) or inside the persistent kernel below.
-template <int MODE, int BM, int CB, bool PERS>
+// per-step launch (PERS = false) or inside the persistent kernel below.  RR:
+// the tile's R rows stay in LDS for the whole layer (loaded at step 0; the
+// persistent form in f16 mode with one phase per step only).
+template <int MODE, int BM, int CB, bool PERS, bool RR = false>
 __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
-  typedef DmaCfg<MODE, BM, CB> C;
+  static_assert(!RR || (PERS && MODE == 1), "resident R: persistent form, f16 mode");
+  typedef DmaCfg<MODE, BM, CB, RR> C;
   typedef typename C::Geo Geo;
   typedef typename Geo::RT RT;
   constexpr int KC = Geo::KC, ASEGS = Geo::ASEGS, BELEMS = Geo::BELEMS;
@@ -456,6 +463,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[NS > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char st3[NS > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char rres[RR ? kRresBytes : 16];
   __shared__ int len_s[BM];
   __shared__ int any_s;
 
@@ -559,10 +567,32 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
           const int k = k0 + (bseg0 ^ rr) * BELEMS;
           off = k < H ? brow[cb][i] + unsigned(k) * BES : kOutOfRange;
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, RNN_LDS_PTR(st + C::A_BYTES + ((wave + 4 * cb) * 16 + 4 * i) * 256), 16, off, 0, 0, 0);
+        if constexpr (!RR)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, RNN_LDS_PTR(st + C::A_BYTES + ((wave + 4 * cb) * 16 + 4 * i) * 256), 16, off, 0, 0, 0);
       }
   };
+  // resident R: chunk kc, column block ci at rres + (kc * ncb + ci) * 4096, in
+  // the layout of a chunk's R part; loaded before the first chunks, so the
+  // chunk waits (the counter retires in order) cover it
+  if constexpr (RR) {
+    if (s == 0) {
+      for (int kc = 0; kc < nk; ++kc)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int ci = wave + 4 * cb;
+          if (ci >= ncb) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * i + (lane >> 4);
+            const int k = kc * KC + (bseg0 ^ rr) * BELEMS;
+            const unsigned off = k < H ? brow[cb][i] + unsigned(k) * BES : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, RNN_LDS_PTR(rres + ((kc * ncb + ci) * 16 + 4 * i) * 256), 16,
+                                                     off, 0, 0, 0);
+          }
+        }
+    }
+  }
 
   // lengths of the tile's rows (wave 0); the load overlaps the first chunks
   int lv = 0;
@@ -672,12 +702,17 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
           }
     } else {
       hx8 bv[CB][4];
+      // resident R: this chunk's blocks (chunks past the end read the last
+      // one, against zero h; a block past the tile reads block 0, dropped)
+      const unsigned char* Rb = Bs;
+      if constexpr (RR) Rb = rres + (kc < nk ? kc : nk - 1) * ncb * 4096;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb) {
+        const int ci = RR && wave + 4 * cb >= ncb ? 0 : wave + 4 * cb;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          bv[cb][kk] =
-              *reinterpret_cast<const hx8*>(Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * q + kk) ^ r16) << 4));
+          bv[cb][kk] = *reinterpret_cast<const hx8*>(Rb + (ci * 16 + r16) * 256 + (((4 * q + kk) ^ r16) << 4));
+      }
       // step kk takes the 8-element k group 4q + kk of both halves of h and
       // of R (the same k for both operands)
       hx8 ah[NBI][4], al[NBI][4];
@@ -760,7 +795,7 @@ struct PersDmaArgs {
 
 constexpr long kFlagSpinLimit = 1l << 22;
 
-template <int MODE, int BM, int CB>
+template <int MODE, int BM, int CB, bool RR>
 __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p) {
   __shared__ int abort_s;
   const int gx = int(gridDim.x);
@@ -790,8 +825,8 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
           return;
         }
       }
-      if (ph == 0) dma_step<MODE, BM, CB, true>(p.ph[0], s);
-      else dma_step<MODE, BM, CB, true>(p.ph[1], s);
+      if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s);
+      else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s);
       // every state store of this workgroup has completed before the flag
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
       __syncthreads();
@@ -821,11 +856,11 @@ static hipError_t launch_bm(const MfmaStepArgs& m, hipStream_t s) {
 }
 
 // The persistent form: one column split for both phases (the wider one).
-template <int MODE, int BM, int CB>
+template <int MODE, int BM, int CB, bool RR = false>
 static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
   const StepArgs& a = pa.ph[0].a;
   const dim3 grid(unsigned((a.H + pa.ph[0].UJ - 1) / pa.ph[0].UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
-  auto kern = step_dma_pers_kernel<MODE, BM, CB>;
+  auto kern = step_dma_pers_kernel<MODE, BM, CB, RR>;
   PersDmaArgs arg = pa;
   // RNN_PLAIN_LAUNCH=1: the same grid without the cooperative API, after a
   // host check that every workgroup fits on the chip at once (for profilers
@@ -850,8 +885,34 @@ static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), grid, dim3(kMThreads), args, 0u, s);
 }
 
+// Resident R (f16 mode, one phase per step, 16 or 32 batch rows): the
+// tile's R rows for every k chunk fit kRresBytes, and the epilogue planes fit
+// a slot that holds h alone.  RNN_MFMA_RRES=0 turns it off.
+template <int MODE, int BM>
+static bool rres_fits(const PersDmaArgs& pa, int* cb) {
+  if constexpr (MODE != 1 || BM > 32) {
+    return false;
+  } else {
+    if (const char* e = std::getenv("RNN_MFMA_RRES"))
+      if (std::atoi(e) == 0) return false;
+    if (pa.P != 1) return false;
+    const MfmaStepArgs& m = pa.ph[0];
+    const int ncb = (m.Gp * m.UJ) >> 4;
+    const int nk = (m.a.H + DmaGeo<1>::KC - 1) / DmaGeo<1>::KC;
+    if (int64_t(nk) * ncb * 4096 > kRresBytes || ncb > 8) return false;
+    const int planes = (m.Gp + epi_state_planes(m.a.cell, m.a.lbr, m.phase)) * BM * m.UJ * 4;
+    *cb = ncb > 4 ? 2 : 1;
+    return planes <= (*cb == 1 ? DmaCfg<1, BM, 1, true>::STAGE : DmaCfg<1, BM, 2, true>::STAGE);
+  }
+}
+
 template <int MODE, int BM>
 static hipError_t launch_pers_bm(const PersDmaArgs& pa, hipStream_t s) {
+  int cb = 1;
+  if constexpr (MODE == 1 && BM <= 32) {
+    if (rres_fits<MODE, BM>(pa, &cb))
+      return cb == 1 ? launch_pers_cfg<MODE, BM, 1, true>(pa, s) : launch_pers_cfg<MODE, BM, 2, true>(pa, s);
+  }
   bool two = false;
   for (int ph = 0; ph < pa.P; ++ph) {
     const MfmaStepArgs& m = pa.ph[ph];

@@ -396,6 +396,33 @@ def test_persistent_matrix_step(cell, dtype, direction, layout, opt, B, H, tile,
                                                  f"B{B}/H{H}/{tile}/split{split}")
 
 
+# The persistent matrix-core step with R resident in LDS (f16 mode, one
+# phase per step): loaded once per layer, read in the same layout and order
+# as the streamed chunks, so the outputs must be bit-identical to the
+# streamed form (RNN_MFMA_RRES=0), and within the bar of the oracle.
+RRES = [("LSTM", 0, 16, 64, 0, 1), ("LSTM", 1, 16, 200, 1, 0), ("GRU", 1, 32, 96, 0, 1), ("RNN", 0, 20, 1000, 1, 0),
+        ("LSTM", 1, 40, 136, 0, 1)]
+
+
+@pytest.mark.parametrize("cell,opt,B,H,layout,bidir", RRES, ids=[f"{c}-{o}-B{b}-H{h}-L{l}-{d}" for c, o, b, h, l, d in RRES])
+def test_persistent_matrix_step_resident_r(cell, opt, B, H, layout, bidir, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=7, batch=B, input=24, hidden=H, direction="bidirectional" if bidir else "forward",
+                     layout=layout, dtype="f16", linear_before_reset=opt if cell == "GRU" else 0,
+                     input_forget=opt if cell == "LSTM" else 0, init_h=True, init_c=cell == "LSTM", lens=True,
+                     peephole=cell == "LSTM", clip=2.0, outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    inp = make_inputs(spec, 71, Dists(sequence_lens=("I", 0, 7), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    note(f"case resident R {cell}/opt{opt}/B{B}/H{H}/L{layout}/bidir{bidir}")
+    got = check(spec, inp, engine="persistent", what=f"resident R {cell} B{B} H{H}")
+    res = gpu_layer(spec, inp, engine="persistent")
+    monkeypatch.setenv("RNN_MFMA_RRES", "0")
+    streamed = gpu_layer(spec, inp, engine="persistent")
+    for n in res:
+        assert np.array_equal(res[n].view(np.uint8), streamed[n].view(np.uint8)), f"{n}: resident R differs"
+
+
 def test_large_batch_general_activations():
     """The matrix-core step kernel with non-default activations (f16 tensors
     then take the f32 path, f32 tensors always do)."""
