@@ -222,12 +222,79 @@ __device__ __forceinline__ void fallback_direction(const StepArgs& a, int d) {
     }
 }
 
+// Staggered polling, for a few words per polling thread (the words
+// ptid + i * kPollThreads): two batches of loads of the thread's words
+// are kept in flight, the second issued about half a load round trip after
+// the first; each batch is checked when it returns and reissued at once, so a
+// word that lands is seen within about half a round trip instead of a whole
+// one.  The loads are unconditional (a slot without a wanted word loads word
+// 0 and ignores it), which keeps each batch's wait an exact count of the
+// younger batch.  On C2 this took the layer from 269 to 199 us; a pause
+// between the rounds of a single batch made it slower, so what counts is how
+// soon a landed word is seen.  With many words per thread the doubled polling
+// traffic swamps the memory system (22 words per thread: 3.6 times slower),
+// and variants for more slots cost every kernel registers, so larger layers
+// keep one batch at a time.
+constexpr int kPollStagger = 32;   // s_sleep units of 64 cycles: about 0.85 us
+
+// One batch row of up to 2 * kPollThreads units (the f32 copy of h is then
+// h itself): polling thread t watches words t and t + kPollThreads.
+__device__ __forceinline__ int stage_words_row(const unsigned long long* src, float* hs, unsigned tag, int H,
+                                               unsigned amask, int ptid) {
+  const int e0 = ptid, e1 = ptid + kPollThreads;
+  const bool w0 = e0 < H && (amask & 1u), w1 = e1 < H && (amask & 1u);
+  const unsigned long long* p0 = src + (w0 ? e0 : 0);
+  const unsigned long long* p1 = src + (w1 ? e1 : 0);
+  unsigned long long a0 = load_word(p0), a1 = load_word(p1);
+  __builtin_amdgcn_s_sleep(kPollStagger);
+  unsigned long long b0 = load_word(p0), b1 = load_word(p1);
+  bool d0 = !w0, d1 = !w1;
+  unsigned v0 = 0, v1 = 0;
+  int fail = 0;
+  for (long round = 0;; ++round) {
+    if (!d0 && static_cast<unsigned>(a0 >> 32) == tag) {
+      v0 = static_cast<unsigned>(a0);
+      d0 = true;
+    }
+    if (!d1 && static_cast<unsigned>(a1 >> 32) == tag) {
+      v1 = static_cast<unsigned>(a1);
+      d1 = true;
+    }
+    if (d0 && d1) break;
+    a0 = load_word(p0);
+    a1 = load_word(p1);
+    if (!d0 && static_cast<unsigned>(b0 >> 32) == tag) {
+      v0 = static_cast<unsigned>(b0);
+      d0 = true;
+    }
+    if (!d1 && static_cast<unsigned>(b1 >> 32) == tag) {
+      v1 = static_cast<unsigned>(b1);
+      d1 = true;
+    }
+    if (d0 && d1) break;
+    b0 = load_word(p0);
+    b1 = load_word(p1);
+    if (round > kSpinLimit) {
+      fail = 1;
+      break;
+    }
+  }
+  if (w0) hs[e0] = __uint_as_float(v0);
+  if (w1) hs[e1] = __uint_as_float(v1);
+  return fail;
+}
+
 // Whole stage, run by the polling waves only (ptid = thread index among
-// them): the first chunk uses the precomputed map `m0`; further chunks (more
-// than kChunk words per polling thread) are mapped on the fly.
+// them): staggered polling for one batch row of up to 384 units;
+// otherwise the first chunk from the precomputed map `m0` and further chunks
+// mapped on the fly, one batch of loads at a time.
 template <int NB, bool MF>
 __device__ __forceinline__ int stage_words(const unsigned long long* src, void* hs, unsigned tag, int H, int HS,
                                            unsigned amask, const WordMap& m0, int ptid) {
+  // (compiled for one batch row only: any inlined variant moves the code and
+  // registers of the other instances too, and cost C3 5 %)
+  if constexpr (NB == 1 && !MF)
+    if (H <= 2 * kPollThreads) return stage_words_row(src, static_cast<float*>(hs), tag, H, amask, ptid);
   int fail = 0;
   const int lo = NB * HS;
   WordPoll w;
