@@ -34,8 +34,11 @@
 // The k index is permuted inside a chunk (lane group q of an operand takes a
 // contiguous quarter of the chunk), identically for h and R, so each lane
 // reads whole 16-byte segments; a sum over a permuted k range is the same sum.
+#include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
+#include "residency.h"
 #include "step_mfma.h"
 
 namespace rnnhip {
@@ -246,7 +249,7 @@ __device__ __forceinline__ float widen(unsigned v, int odd) {
 
 // Element e of the tile is row e >> ujs, unit e & (UJ - 1); elements from
 // n_el on do not exist.
-template <typename RT>
+template <typename RT, bool INIT = false>
 __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, int e, int n_el, int ujs, int b0, int j0,
                                            EpiIn& o) {
   const int H = c.H, s = c.s;
@@ -255,6 +258,24 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
   const int L = e < n_el ? len_s[r] : 0;
   o.len = L;
   o.live = b < c.B && j < H && s < L;
+  // INIT: every field defined on every path, so that the struct stays in
+  // registers.  In the persistent kernel, fields left unset on some paths
+  // kept the state loads in scratch memory, with a wait for each right where
+  // it was issued (C4 1.71 -> 1.61 ms with INIT); in the per-step kernel
+  // the same initialisation cost C5 2 %.
+  if constexpr (INIT) {
+    o.cprev = 0.f;
+    o.hprev = 0.f;
+    o.z = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      o.xv[gi] = 0.f;
+      o.wb[gi] = 0u;
+      o.rb[gi] = 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) o.pp[k] = 0u;
+  }
   if (j >= H) return;
   // the unit's biases and peepholes, also for a row that does not run: the
   // thread's later elements (same unit) take them from here
@@ -631,7 +652,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   const EpiCtx ctx = epi_context<RT>(m, d, s, PERS);
   const int n_el = BM * UJ;   // a multiple of the workgroup size
   EpiIn first;
-  epi_gather<RT>(ctx, len_s, tid, n_el, ujs, b0, j0, first);
+  epi_gather<RT, PERS>(ctx, len_s, tid, n_el, ujs, b0, j0, first);
 
   // chunk kc lives in slot kc % NS; the loop is unrolled over the slots so
   // that every slot is a fixed LDS object.  The chunk count is rounded up to
@@ -776,8 +797,8 @@ __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
   dma_step<MODE, BM, CB, false>(m, m.step);
 }
 
-// Every step in one cooperative launch (all tiles resident together).  A
-// workgroup keeps its tile for the whole layer, so the R rows it streams stay
+// Every step in one launch (all tiles resident together, settled as in
+// residency.h).  A workgroup keeps its tile for the whole layer, so the R rows it streams stay
 // in its XCD's L2 from one step to the next instead of being fetched again
 // after each kernel boundary.  Between phases, each workgroup publishes the
 // count of phases it has finished in its own flag (a device-scope store after
@@ -790,13 +811,30 @@ struct PersDmaArgs {
   MfmaStepArgs ph[2];   // per phase (a GRU with linear_before_reset = 0 has two)
   int P;                // phases per step
   int* flags;           // one per workgroup: phases finished; zeroed by the state setup
-  int* status;          // set to 1 if a wait ran past its bound
+  int* status;          // [0] set to 1 if a wait ran past its bound; [1], [2] residency (residency.h)
+  int fallback;         // > 0: take the fallback with this many workgroups (tests)
 };
 
 constexpr long kFlagSpinLimit = 1l << 22;
 
 template <int MODE, int BM, int CB, bool RR>
 __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p) {
+  // launched plainly: every workgroup running (GO), or one workgroup per
+  // direction runs the layer on the per-step engine's state (residency.h)
+  __shared__ int coop_dec, coop_ticket;
+  if (threadIdx.x == 0) {
+    const int t = arrive_ticket(p.status + 1);
+    coop_dec = arrive_decide(p.status + 1, int(gridDim.x * gridDim.y * gridDim.z), p.fallback, t);
+    coop_ticket = t;
+  }
+  __syncthreads();
+  if (__builtin_expect(coop_dec != 1, 0)) {
+    typedef typename std::conditional<MODE == 1, half_t, float>::type T;   // the tensors' element type
+    const int cnt = coop_dec >> 8;
+    if (coop_ticket < cnt)
+      for (int dd = coop_ticket; dd < p.ph[0].a.D; dd += cnt) fallback_direction<T>(p.ph[0].a, dd);
+    return;
+  }
   __shared__ int abort_s;
   const int gx = int(gridDim.x);
   const int row = int(blockIdx.y + gridDim.y * blockIdx.z);   // batch tile and direction
@@ -862,14 +900,11 @@ static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
   const dim3 grid(unsigned((a.H + pa.ph[0].UJ - 1) / pa.ph[0].UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
   auto kern = step_dma_pers_kernel<MODE, BM, CB, RR>;
   PersDmaArgs arg = pa;
-  // RNN_PLAIN_LAUNCH=1: the same grid without the cooperative API, after a
-  // host check that every workgroup fits on the chip at once (for profilers
-  // that fail on cooperative launches)
-  static const bool plain = [] {
-    const char* e = std::getenv("RNN_PLAIN_LAUNCH");
-    return e && e[0] == '1';
-  }();
-  if (plain) {
+  // A plain launch after a host check that every workgroup fits on the device
+  // at once; the kernel settles residency itself (residency.h).
+  // RNN_COOPERATIVE_LAUNCH=1 takes the cooperative launch instead.
+  const char* coop_env = std::getenv("RNN_COOPERATIVE_LAUNCH");
+  if (!(coop_env && coop_env[0] == '1')) {
     int per_cu = 0, dev = 0, cus = 0;
     hipError_t e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kMThreads,
@@ -932,6 +967,7 @@ hipError_t launch_step_dma_persistent(const MfmaStepArgs* ph, int P, int bm, int
   pa.P = P;
   pa.flags = flags;
   pa.status = status;
+  if (const char* e = std::getenv("RNN_PERSISTENT_FALLBACK")) pa.fallback = std::max(0, std::atoi(e));
   if (mode == 1)
     return bm == 64 ? launch_pers_bm<1, 64>(pa, s) : bm == 32 ? launch_pers_bm<1, 32>(pa, s)
                                                       : launch_pers_bm<1, 16>(pa, s);

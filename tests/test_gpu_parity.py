@@ -423,6 +423,27 @@ def test_persistent_matrix_step_resident_r(cell, opt, B, H, layout, bidir, monke
         assert np.array_equal(res[n].view(np.uint8), streamed[n].view(np.uint8)), f"{n}: resident R differs"
 
 
+# The persistent matrix-core step's fallback (its grid not all running at
+# once, forced with RNN_PERSISTENT_FALLBACK = k): one workgroup per direction
+# runs the layer on the per-step engine's state.
+MFALL = [("LSTM", 1, "f16", 0), ("GRU", 0, "f16", 1), ("RNN", 0, "f32", 0)]
+
+
+@pytest.mark.parametrize("cell,opt,dtype,layout", MFALL, ids=[f"{c}-{o}-{d}-L{l}" for c, o, d, l in MFALL])
+@pytest.mark.parametrize("forced", ["1", "2"])
+def test_persistent_matrix_step_fallback(cell, opt, dtype, layout, forced, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=6, batch=20, input=24, hidden=40, direction="bidirectional", layout=layout,
+                     dtype=dtype, linear_before_reset=opt if cell == "GRU" else 0,
+                     input_forget=opt if cell == "LSTM" else 0, init_h=True, init_c=cell == "LSTM", lens=True,
+                     peephole=cell == "LSTM", clip=2.0, outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    inp = make_inputs(spec, 83, Dists(sequence_lens=("I", 0, 6), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    monkeypatch.setenv("RNN_PERSISTENT_FALLBACK", forced)
+    check(spec, inp, engine="persistent", what=f"matrix-core fallback {forced} {cell}")
+
+
 def test_large_batch_general_activations():
     """The matrix-core step kernel with non-default activations (f16 tensors
     then take the f32 path, f32 tensors always do)."""
