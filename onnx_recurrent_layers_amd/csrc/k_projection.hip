@@ -511,14 +511,16 @@ static hipError_t launch_tile(const ProjArgs& a, const SetupArgs& sa, int setup_
   return hipGetLastError();
 }
 
-hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s);
+hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, int dtype,
+                                 hipStream_t s);
 
 hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s) {
   const int64_t n_state = int64_t(sa.D) * sa.B * sa.H;
   const int setup_blocks = n_state > 0 ? int(std::min<int64_t>((n_state + 255) / 256, 1024)) : 0;
-  // large f16 layers: 256x256 tiles loaded straight into LDS (k_projection_lds.hip)
-  if (dtype == RNN_DTYPE_F16 && a.M > 0 && a.N > 0) {
-    const hipError_t e = launch_projection_lds(a, sa, setup_blocks, s);
+  // large f16 layers, and large f32 layers on the bf16 matrix cores: 256x256
+  // tiles loaded straight into LDS (k_projection_lds.hip)
+  if ((dtype == RNN_DTYPE_F16 || (dtype == RNN_DTYPE_F32 && a.f32_split)) && a.M > 0 && a.N > 0) {
+    const hipError_t e = launch_projection_lds(a, sa, setup_blocks, dtype, s);
     if (e != hipErrorNotSupported) return e;
   }
   // 128x128 tiles when they still give every compute unit a workgroup, else

@@ -16,6 +16,17 @@
 // different bank groups.  Inside a chunk lane group g of an operand takes k
 // 16g..16g+15 (for both operands, so each dot product is the same sum).
 //
+// f32 layers whose projection runs on the bf16 matrix cores (three split
+// products) use the same tiles with f32 operands: a 64-byte row then holds 16
+// values, so a chunk covers k 16 and has the same LDS layout, loads and waits.
+// Each lane reads the 8 values of its lane group (k 8g..8g+7) and splits them
+// on the way into registers, hi = bf16(x) and lo = bf16(x - hi) (round to
+// nearest even; x - hi is exact in f32), and each 32x32 block takes
+// lo_x.hi_w + hi_x.lo_w + hi_x.hi_w with v_mfma_f32_32x32x16_bf16, f32
+// accumulation: bf16 products are exact in f32, and what the split drops is
+// below 2^-16 of each |x.w|.  Splitting as the operands are read, not as they
+// are stored, is what lets them go straight into LDS.
+//
 // The grid is laid out for the eight XCDs: workgroup i runs on XCD i % 8, and
 // the tiles of one XCD are consecutive in n within an m row, so neighbouring
 // tiles of an XCD share their X panel in that XCD's L2.  Column tiles inside
@@ -31,12 +42,14 @@ namespace rnnhip {
 namespace {
 
 typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 256;          // rows and columns of an output tile
-constexpr int kKC = 32;             // k per chunk
+constexpr int kRowBytes = 64;       // bytes of one operand row of a chunk: k 32 (f16) or 16 (f32)
 constexpr int kNS = 4;              // chunks resident
-constexpr int kOpBytes = kTile * kKC * 2;   // one operand of one chunk (16 KiB)
+constexpr int kOpBytes = kTile * kRowBytes;  // one operand of one chunk (16 KiB)
 constexpr int kLoads = kOpBytes / 1024 / 4; // loads per wave per operand per chunk (4)
 constexpr unsigned kOOB = 0x80000000u;      // beyond every resource used here
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit data format (gfx9 family)
@@ -51,13 +64,29 @@ __device__ __forceinline__ void chunk_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// hi = bf16(x), lo = bf16(x - hi) of eight values
+__device__ __forceinline__ void split8(const f32x4 p, const f32x4 q, bx8& hi, bx8& lo) {
+  const float x[8] = {p[0], p[1], p[2], p[3], q[0], q[1], q[2], q[3]};
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    const __bf16 h = __bf16(x[z]);
+    hi[z] = h;
+    lo[z] = __bf16(x[z] - float(h));
+  }
+}
+
 }  // namespace
 
 struct TileMap {
   int mt, nct, tiles_per_dir, per_xcd, sb0, nskip;
 };
 
+// T = half_t: f16 operands; T = float: f32 operands split into bf16 halves.
+template <typename T>
 __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupArgs sa, TileMap tm, int gemm_blocks) {
+  constexpr int ES = int(sizeof(T));          // element bytes
+  constexpr int KC = kRowBytes / ES;          // k per chunk
+  constexpr int SEGE = 16 / ES;               // elements of a 16-byte segment
   // one LDS object per operand of each resident chunk (the compiler then
   // keeps its waits for the loads into one chunk apart from the reads of
   // another)
@@ -65,7 +94,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
   __shared__ __attribute__((aligned(1024))) unsigned char wb0[kOpBytes], wb1[kOpBytes], wb2[kOpBytes], wb3[kOpBytes];
 
   if (int(blockIdx.x) >= gemm_blocks) {
-    setup_state<half_t>(sa, int(blockIdx.x) - gemm_blocks, int(gridDim.x) - gemm_blocks);
+    setup_state<T>(sa, int(blockIdx.x) - gemm_blocks, int(gridDim.x) - gemm_blocks);
     return;
   }
   // XCD-aware tile order: workgroup i -> tile (i % 8) * per_xcd + i / 8
@@ -79,10 +108,9 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.X), 0, int(a.S * a.B * a.K * 2), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.X), 0, int(a.S * a.B * a.K * ES), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<half_t*>(static_cast<const half_t*>(a.W) + int64_t(d) * a.N * a.K), 0, int(a.N * a.K * 2),
-      kRsrcWord3);
+      const_cast<T*>(static_cast<const T*>(a.W) + int64_t(d) * a.N * a.K), 0, int(a.N * a.K * ES), kRsrcWord3);
 
   // this lane's rows: load i of the wave covers tile rows (wave*kLoads + i)*16 .. +16,
   // lane l row +l/4, slot l%4 holding segment slot ^ ((row >> 2) & 3)
@@ -98,16 +126,16 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
       const int64_t tt = m / a.B;
       xr = (m - tt * a.B) * a.S + tt;
     }
-    xrow[i] = m < a.M ? unsigned(xr * K * 2) : kOOB;
-    wrow[i] = n < a.N ? unsigned(n * K * 2) : kOOB;
+    xrow[i] = m < a.M ? unsigned(xr * K * ES) : kOOB;
+    wrow[i] = n < a.N ? unsigned(n * K * ES) : kOOB;
   }
   auto fetch = [&](int kc, unsigned char* sa_, unsigned char* sb_) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int k = kc * kKC + seg[i] * 8;
+      const int k = kc * KC + seg[i] * SEGE;
       // a row outside the matrix starts at the out-of-range marker, so row + k stays out of range
-      const unsigned ox = k < K ? xrow[i] + unsigned(k) * 2u : kOOB;
-      const unsigned ow = k < K ? wrow[i] + unsigned(k) * 2u : kOOB;
+      const unsigned ox = k < K ? xrow[i] + unsigned(k) * unsigned(ES) : kOOB;
+      const unsigned ow = k < K ? wrow[i] + unsigned(k) * unsigned(ES) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, RNN_LDS_PTR(sa_ + (wave * kLoads + i) * 1024), 16, ox, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, RNN_LDS_PTR(sb_ + (wave * kLoads + i) * 1024), 16, ow, 0, 0, 0);
     }
@@ -125,7 +153,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
 
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
-  const int nk = (K + kKC - 1) / kKC;
+  const int nk = (K + KC - 1) / KC;
 #pragma unroll
   for (int c = 0; c < kNS - 1; ++c) fetch(c, slot_a(c), slot_b(c));
   // chunk kc lives in slot kc % 4; the loop is unrolled over the slots so that
@@ -138,6 +166,35 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
       fetch(kc + kNS - 1, slot_a((u + kNS - 1) % kNS), slot_b((u + kNS - 1) % kNS));
       const unsigned char* As = slot_a(u);
       const unsigned char* Bs = slot_b(u);
+      if constexpr (ES == 4) {
+        // lane group g: segments 2g and 2g+1 of each row (k 8g..8g+7)
+        bx8 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 128 + i * 32 + r32;
+          const unsigned char* rp = As + row * 64;
+          const int sw = (row >> 2) & 3;
+          split8(*reinterpret_cast<const f32x4*>(rp + (((2 * g) ^ sw) << 4)),
+                 *reinterpret_cast<const f32x4*>(rp + (((2 * g + 1) ^ sw) << 4)), ah[i], al[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = wn * 128 + j * 32 + r32;
+          const unsigned char* rp = Bs + row * 64;
+          const int sw = (row >> 2) & 3;
+          split8(*reinterpret_cast<const f32x4*>(rp + (((2 * g) ^ sw) << 4)),
+                 *reinterpret_cast<const f32x4*>(rp + (((2 * g + 1) ^ sw) << 4)), bh[j], bl[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+          }
+        continue;
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int s = 2 * g + kk;
@@ -176,13 +233,16 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
       }
 }
 
-// Takes the layer when the operands are f16 rows of whole 16-byte segments,
-// every byte offset fits 32 bits and the tiles fill the chip; otherwise
-// reports hipErrorNotSupported and the caller uses the other kernel.
-hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, hipStream_t s) {
-  if (a.K % 8 != 0 || reinterpret_cast<uintptr_t>(a.X) % 16 != 0 || reinterpret_cast<uintptr_t>(a.W) % 16 != 0)
+// Takes the layer when the operands are rows of whole 16-byte segments (f16,
+// or f32 split into bf16 halves), every byte offset fits 31 bits and the
+// tiles fill the chip; otherwise reports hipErrorNotSupported and the caller
+// uses the other kernels.
+hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, int dtype,
+                                 hipStream_t s) {
+  const int es = dtype == RNN_DTYPE_F32 ? 4 : 2;
+  if (a.K % (16 / es) != 0 || reinterpret_cast<uintptr_t>(a.X) % 16 != 0 || reinterpret_cast<uintptr_t>(a.W) % 16 != 0)
     return hipErrorNotSupported;
-  if (a.S * a.B * a.K * 2 >= int64_t(kOOB) || a.N * a.K * 2 >= int64_t(kOOB)) return hipErrorNotSupported;
+  if (a.S * a.B * a.K * es >= int64_t(kOOB) || a.N * a.K * es >= int64_t(kOOB)) return hipErrorNotSupported;
   TileMap tm{};
   tm.mt = int((a.M + kTile - 1) / kTile);
   const int nt = int((a.N + kTile - 1) / kTile);
@@ -203,8 +263,12 @@ hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int set
   tm.per_xcd = int((tiles + 7) / 8);
   const int gemm_blocks = 8 * tm.per_xcd;
   if (int64_t(gemm_blocks) + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(projection_lds_kernel, dim3(unsigned(gemm_blocks + setup_blocks)), dim3(256), 0, s, a, sa, tm,
-                     gemm_blocks);
+  if (dtype == RNN_DTYPE_F32)
+    hipLaunchKernelGGL(projection_lds_kernel<float>, dim3(unsigned(gemm_blocks + setup_blocks)), dim3(256), 0, s, a,
+                       sa, tm, gemm_blocks);
+  else
+    hipLaunchKernelGGL(projection_lds_kernel<half_t>, dim3(unsigned(gemm_blocks + setup_blocks)), dim3(256), 0, s, a,
+                       sa, tm, gemm_blocks);
   return hipGetLastError();
 }
 

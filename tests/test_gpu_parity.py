@@ -125,6 +125,36 @@ def test_projection_scratch_bf16x3(layout, S, B, I, H, monkeypatch):
         assert np.max(err) <= 1e-4
 
 
+# The same split products in the 256x256 tiles loaded straight into LDS (f32
+# operands split as they are read), forced onto small layers: ragged M, N and
+# K tails, layout 1, the skipped f block.
+@pytest.mark.parametrize("layout,cell,input_forget,S,B,I,H", [
+    (0, "GRU", 0, 17, 19, 200, 90), (1, "LSTM", 1, 9, 70, 136, 256), (0, "RNN", 0, 3, 40, 1024, 300)])
+def test_projection_lds_bf16x3(layout, cell, input_forget, S, B, I, H, monkeypatch):
+    import torch
+    monkeypatch.setenv("RNN_F32_SPLIT", "1")
+    monkeypatch.setenv("RNN_PROJ_LDS_MIN_TILES", "1")
+    spec = LayerSpec(cell, seq=S, batch=B, input=I, hidden=H, layout=layout, dtype="f32", input_forget=input_forget,
+                     direction="bidirectional", outputs=("Y_h",))
+    inp = make_inputs(spec, 12)
+    note(f"case projection-lds bf16x3 {cell} L{layout} S{S} B{B} I{I} H{H}")
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    D, G = 2, spec.gates
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
+    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
+    A = X.reshape(S * B, I)
+    for d in range(D):
+        ref = oracle.projection(A, inp["W"][d])
+        bound = 2.0 ** -15 * (np.abs(A.astype(np.float64)) @ np.abs(inp["W"][d].astype(np.float64)).T) + 1e-30
+        cols = np.ones(G * H, bool)
+        if input_forget:
+            cols[2 * H:3 * H] = False     # the f block is not computed
+        err = np.abs(xw[d][:, cols].astype(np.float64) - ref[:, cols])
+        assert np.all(err <= bound[:, cols]), (d, float(np.max(err / bound[:, cols])))
+    check(spec, inp, engine="launch", twice=False, what=f"projection-lds bf16x3 {cell}")
+
+
 @pytest.mark.parametrize("cell", ["LSTM", "GRU", "RNN"])
 def test_layers_with_bf16x3_projection(cell, monkeypatch):
     """Whole f32 layers with the split projection, on both engines."""
