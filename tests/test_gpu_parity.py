@@ -617,3 +617,62 @@ def test_full_config(name, over):
         ref = oracle_rows(spec, inp, rows, outputs=spec.outputs)
         rep = compare(spec, select_rows(spec, got, rows), ref, what=name)
     note(f"{name} {over}: " + ", ".join(f"{k} abs {v[0]:.3g} scaled {v[1]:.3g}" for k, v in rep.items()))
+
+
+# ---------------------------------------------------------------------------
+# stacked layers and streaming continuation
+# ---------------------------------------------------------------------------
+def test_stacked_layers_without_transpose():
+    """A bidirectional layout-1 layer's Y [B, S, 2, H] is the next layer's X
+    [B, S, 2H] as it lies in memory: the second layer reads the first one's
+    output buffer in place, no transpose and no copy."""
+    import onnx_recurrent_layers_amd as rl
+    B, S, H1 = 3, 9, 12
+    s1 = LayerSpec("LSTM", seq=S, batch=B, input=10, hidden=H1, direction="bidirectional", layout=1, dtype="f32",
+                   init_h=True, init_c=True, peephole=True, outputs=("Y",))
+    in1 = make_inputs(s1, 91)
+    y1 = rl.run(s1, in1, engine="persistent", outputs=("Y",))["Y"]
+    assert tuple(y1.shape) == (B, S, 2, H1)
+    compare(s1, {"Y": y1.cpu().numpy()}, oracle.run(s1, in1, outputs=("Y",)), what="stacked layer 1")
+    for engine in ("persistent", "launch"):
+        s2 = LayerSpec("GRU", seq=S, batch=B, input=2 * H1, hidden=8, direction="bidirectional", layout=1,
+                       dtype="f32", linear_before_reset=1, outputs=("Y", "Y_h"))
+        in2 = make_inputs(s2, 92)
+        dev = rl.to_device({k: v for k, v in in2.items() if k != "X"})
+        dev["X"] = y1.view(B, S, 2 * H1)   # the first layer's output, read in place
+        got = rl.run(s2, dev, engine=engine, outputs=s2.outputs)
+        ref = oracle.run(s2, {**in2, "X": y1.view(B, S, 2 * H1).cpu().numpy()}, outputs=s2.outputs)
+        compare(s2, {k: v.cpu().numpy() for k, v in got.items()}, ref, what=f"stacked layer 2 {engine}")
+
+
+@pytest.mark.parametrize("cell,engine", [("LSTM", "persistent"), ("GRU", "launch"), ("RNN", "persistent"),
+                                         ("LSTM", "launch")])
+def test_streaming_continuation(cell, engine):
+    """A sequence run in two pieces, the second starting from the first's
+    Y_h (and Y_c), gives the same bits as one run over the whole sequence: the
+    projection of a row and the arithmetic of a step do not depend on the
+    sequence length, and f32 final states carry the state exactly."""
+    import torch
+    import onnx_recurrent_layers_amd as rl
+    S1, S2, B = 5, 7, 4 if engine == "persistent" else 19
+    lstm = cell == "LSTM"
+    outs = ("Y", "Y_h", "Y_c") if lstm else ("Y", "Y_h")
+
+    def spec(seq):
+        return LayerSpec(cell, seq=seq, batch=B, input=11, hidden=20, direction="forward", layout=0, dtype="f32",
+                         init_h=True, init_c=lstm, peephole=lstm, clip=3.0, outputs=outs)
+
+    full = spec(S1 + S2)
+    inp = make_inputs(full, 93)
+    rf = rl.run(full, inp, engine=engine, outputs=outs)
+    compare(full, {k: v.cpu().numpy() for k, v in rf.items()}, oracle.run(full, inp, outputs=outs),
+            what=f"continuation reference {cell}")
+    ra = rl.run(spec(S1), {**inp, "X": inp["X"][:S1]}, engine=engine, outputs=outs)
+    inb = {**inp, "X": inp["X"][S1:], "initial_h": ra["Y_h"].cpu().numpy()}
+    if lstm:
+        inb["initial_c"] = ra["Y_c"].cpu().numpy()
+    rb = rl.run(spec(S2), inb, engine=engine, outputs=outs)
+    y = torch.cat([ra["Y"], rb["Y"]], dim=0)
+    assert torch.equal(y.view(torch.int32), rf["Y"].view(torch.int32)), f"{cell}: Y differs"
+    for n in outs[1:]:
+        assert torch.equal(rb[n].view(torch.int32), rf[n].view(torch.int32)), f"{cell}: {n} differs"
