@@ -288,6 +288,45 @@ __device__ __forceinline__ float4 ld4(const half_t* p) {
 // order, and sum8 combines the eight partial sums in a fixed tree.  Rows and
 // hs are zero-padded to H4 (a multiple of 32), which adds exact zeros.
 template <typename T, int NB>
+__device__ __forceinline__ void products_ksplit(const T* Rl, int RS, const float* hs, float* rec, int NRNB, int r_lo,
+                                                int r_hi, int H4) {
+  // two groups per row: group rg takes row r_lo + rg % 16 and the 32-wide k
+  // chunks of parity rg / 16; the two partial sums go to rec and rec + NRNB,
+  // and the gate code adds them in that order
+  const int c = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const int r0 = r_lo + (rg & 15), half = rg >> 4;
+  if (r0 >= r_hi) return;
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  const T* row = Rl + r0 * RS;
+#pragma unroll 4
+  for (int k0 = 4 * c + 32 * half; k0 < H4; k0 += 64) {
+    const float4 a0 = ld4(row + k0);
+    const float* hk = hs + k0 * NB;
+    float hv[4 * NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const float4 v = ld4(hk + 4 * q);
+      hv[4 * q] = v.x;
+      hv[4 * q + 1] = v.y;
+      hv[4 * q + 2] = v.z;
+      hv[4 * q + 3] = v.w;
+    }
+    const float ra0[4] = {a0.x, a0.y, a0.z, a0.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] += ra0[i] * hv[i * NB + b];
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float v = sum8(acc[b]);
+    if (c == b) rec[half * NRNB + r0 * NB + b] = v;
+  }
+}
+
+template <typename T, int NB>
 __device__ __forceinline__ void products(const T* Rl, int RS, const float* hs, float* rec, int r_lo, int r_hi,
                                          int H4) {
   const int c = threadIdx.x & 7, rg = threadIdx.x >> 3;
@@ -432,11 +471,16 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   void* hs = smem + r_bytes;
   float* rec = reinterpret_cast<float*>(smem + r_bytes + (MF ? size_t(4) * NB * HS : size_t(4) * NB * H4));
   const int NRNB = p.NR * NB;
+  // the vector-ALU products with at most 16 rows leave half the lane groups
+  // idle: then two groups share each row, one per parity of the 32-wide k
+  // chunks (C2: 204 -> 187 us per layer, the recognizer shape 48/8/192/96:
+  // 214 -> 193 us; needs two chunks at least)
+  const bool ksplit = !MF && p.NR <= 16 && H4 >= 64;
   // recurrent sum of row r, batch row b
   auto recv = [&](int r, int b) {
     const int i = r * NB + b;
     if constexpr (MF) return ((rec[i] + rec[NRNB + i]) + rec[2 * NRNB + i]) + rec[3 * NRNB + i];
-    else return rec[i];
+    else return ksplit ? rec[i] + rec[NRNB + i] : rec[i];
   };
 
   // R rows of this workgroup's units, resident for the whole layer
@@ -560,6 +604,8 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     if constexpr (MF)
       products_mfma<NB>(reinterpret_cast<const half_t*>(Rl), RS, static_cast<const half_t*>(hs), HS, rec, r_lo, r_hi,
                         p.NR, H4);
+    else if (ksplit)
+      products_ksplit<T, NB>(Rl, RS, static_cast<const float*>(hs), rec, NRNB, r_lo, r_hi, H4);
     else
       products<T, NB>(Rl, RS, static_cast<const float*>(hs), rec, r_lo, r_hi, H4);
   };
@@ -669,7 +715,7 @@ size_t lds_bytes(int NR, int H, int esize, int NB, bool mf) {
   const int H4 = (H + 31) & ~31;
   const size_t r = (size_t(NR) * (H4 + 8) * esize + 15) & ~size_t(15);
   if (mf) return r + size_t(4) * NB * (H4 + 8) + size_t(4) * NR * NB * 4;
-  return r + size_t(NB) * H4 * 4 + size_t(NR) * NB * 4;
+  return r + size_t(NB) * H4 * 4 + size_t(2) * NR * NB * 4;
 }
 
 // All activation slots are the cell's ONNX defaults.
