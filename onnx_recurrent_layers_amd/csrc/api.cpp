@@ -170,9 +170,9 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     if (const char* e = std::getenv("RNN_F32_SPLIT")) want = std::atoi(e) != 0;
     p->f32_split_step = want && step_dma_supported(t, 2);
   }
-  // Batches of 16 and more: the matrix-core step, in one cooperative launch
+  // Batches of 16 and more: the matrix-core step, in one persistent launch
   // when its tiles fit the chip (else one launch per step).  The automatic
-  // choice takes the cooperative launch only for f16 layers with the default
+  // choice takes the persistent launch only for f16 layers with the default
   // activations (split h): there it measured faster than one launch per step
   // (LSTM 256/64/1024/1024: 2.41 against 2.53 ms of steps), while for f32
   // layers it measured slower (RNN 1024/256/1024/2048 in bf16 split mode:

@@ -772,8 +772,8 @@ static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStrea
   PersArgs arg = pa;
   // A plain launch after checking on the host that every workgroup fits on
   // the device at once; the kernel itself settles whether they all run
-  // together (see the top of this file).  RNN_COOPERATIVE_LAUNCH=1 takes the
-  // cooperative launch instead (about 18 us more per launch here).
+  // together (residency.h).  RNN_COOPERATIVE_LAUNCH=1 takes the cooperative
+  // launch instead (about 18 us more per launch here).
   const char* coop_env = std::getenv("RNN_COOPERATIVE_LAUNCH");
   if (!(coop_env && coop_env[0] == '1')) {
     int per_cu = 0, dev = 0, cus = 0;

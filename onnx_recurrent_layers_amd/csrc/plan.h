@@ -48,7 +48,7 @@ struct Problem {
   int engine = RNN_ENGINE_LAUNCH;
   bool def_acts = false;  // every activation slot holds the cell's ONNX default
   // persistent engine geometry
-  int pers_blocks = 0;       // workgroups of the cooperative launch
+  int pers_blocks = 0;       // workgroups of the persistent launch
   int pers_units = 0;        // units per workgroup
   int pers_wg_per_dir = 0;
   // the persistent engine in its matrix-core form (batches of 16 and more)
@@ -153,7 +153,7 @@ hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);
 bool mfma_step_supported(const Problem& p);
-// Persistent form of the matrix-core step: one cooperative launch for every
+// Persistent form of the matrix-core step: one launch for every
 // step, at most kPersistentMfmaTiles workgroups (one per compute unit).
 constexpr int kPersistentMfmaTiles = 256;
 bool mfma_persistent_supported(const Problem& p, int* tiles);

@@ -132,7 +132,7 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
 // f32 matrix cores; 1: f16 tensors with the default activations (split h);
 // 2: f32 tensors on the bf16 matrix cores (h and R as bf16 hi/lo planes).
 hipError_t launch_step_dma(const MfmaStepArgs& m, int bm, int mode, hipStream_t s);
-// Every step in one cooperative launch of the same kernel body (`ph`: the
+// Every step in one launch of the same kernel body (`ph`: the
 // arguments of each of the P phases of a step; `flags`: one int per
 // workgroup, zeroed beforehand).  hipErrorNotSupported: the tile's epilogue
 // planes do not fit; the caller then launches per step.

@@ -386,7 +386,7 @@ def test_matrix_step_bf16x3(cell, direction, layout, opt, B, H, tile, acts, monk
     check(spec, inp, engine="launch", what=f"bf16x3 step {cell}/{direction}/L{layout}/opt{opt}/B{B}/H{H}/{tile}")
 
 
-# The persistent form of the matrix-core step (one cooperative launch for
+# The persistent form of the matrix-core step (one launch for
 # every step, batches of 16 and more): the three modes, every cell, both GRU
 # forms (two phases per step), forced tile shapes and column splits, ragged
 # batch and hidden sizes, lengths with 0, both layouts and directions.
@@ -585,7 +585,7 @@ def test_engine_choice_and_plan():
         layer = rl.Layer(spec, engine="auto", device="cuda:0")
         assert layer.plan.engine == rl.ENGINES["persistent"], name
         assert layer.plan.step_launches == 1
-    # C4 (f16, split h): the matrix-core step in one cooperative launch; C5
+    # C4 (f16, split h): the matrix-core step in one persistent launch; C5
     # (f32): one launch per step, unless the persistent engine is asked for
     spec, _ = synth.config("C4")
     layer = rl.Layer(spec, engine="auto", device="cuda:0")
