@@ -305,6 +305,28 @@ def test_persistent_fallback(cell, opt, dtype, layout, forced, monkeypatch):
     assert status == 0 and decision == 1 and arrivals == layer.plan.step_blocks, (status, arrivals, decision)
 
 
+# One batch row on the persistent engine: the staggered polling (hidden sizes
+# up to 384) and the two lane groups per row of the vector-ALU products (16
+# rows or fewer per workgroup, two k chunks or more), for every cell and GRU
+# form, both directions, both dtypes, on both sides of each limit.
+BATCH1 = [(c, o, H) for c, o in (("LSTM", 0), ("LSTM", 1), ("GRU", 0), ("GRU", 1), ("RNN", 0))
+          for H in (32, 40, 64, 300, 400)]
+
+
+@pytest.mark.parametrize("cell,opt,H", BATCH1, ids=[f"{c}-{o}-H{h}" for c, o, h in BATCH1])
+def test_persistent_batch_one(cell, opt, H):
+    import onnx_recurrent_layers_amd as rl
+    for dtype, direction, layout in (("f32", "bidirectional", 0), ("f16", "reverse", 1)):
+        spec = LayerSpec(cell, seq=7, batch=1, input=29, hidden=H, direction=direction, layout=layout, dtype=dtype,
+                         linear_before_reset=opt if cell == "GRU" else 0, input_forget=opt if cell == "LSTM" else 0,
+                         init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM", clip=2.5,
+                         outputs=("Y", "Y_h", "Y_c"))
+        layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+        assert layer.plan.engine == rl.ENGINES["persistent"]
+        inp = make_inputs(spec, 101, Dists(sequence_lens=("I", 1, 7), W=("U", -0.15, 0.15), R=("U", -0.15, 0.15)))
+        check(spec, inp, engine="persistent", what=f"batch one {cell}/opt{opt}/H{H}/{dtype}")
+
+
 LARGE = [(c, d, dt) for c in ("LSTM", "GRU", "RNN") for d in ("forward", "bidirectional") for dt in ("f32", "f16")]
 
 
