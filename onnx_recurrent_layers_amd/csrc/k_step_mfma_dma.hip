@@ -829,7 +829,9 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
   }
   __syncthreads();
   if (__builtin_expect(coop_dec != 1, 0)) {
-    typedef typename std::conditional<MODE == 1, half_t, float>::type T;   // the tensors' element type
+    // the tensors' element type: f16 in mode 1, f32 in modes 0 and 2 (the
+    // launcher refuses any other pairing)
+    typedef typename std::conditional<MODE == 1, half_t, float>::type T;
     const int cnt = coop_dec >> 8;
     if (coop_ticket < cnt)
       for (int dd = coop_ticket; dd < p.ph[0].a.D; dd += cnt) fallback_direction<T>(p.ph[0].a, dd);
@@ -967,6 +969,8 @@ hipError_t launch_step_dma_persistent(const MfmaStepArgs* ph, int P, int bm, int
   pa.P = P;
   pa.flags = flags;
   pa.status = status;
+  // the fallback reads the tensors as f16 in mode 1 and as f32 otherwise
+  if ((mode == 1) != (ph[0].a.dtype == RNN_DTYPE_F16)) return hipErrorNotSupported;
   if (const char* e = std::getenv("RNN_PERSISTENT_FALLBACK")) pa.fallback = std::max(0, std::atoi(e));
   if (mode == 1)
     return bm == 64 ? launch_pers_bm<1, 64>(pa, s) : bm == 32 ? launch_pers_bm<1, 32>(pa, s)
