@@ -157,6 +157,15 @@ CONFIGS = {
                     initial_h=("N", 0.0, 1.0), sequence_lens=("I", 1, 128)),
         seed=3,
         name="biGRU S128 B8 I512 H512 f16 L0 lens"),
+    # the same GRU layer with the reset gate applied after the recurrent
+    # product (linear_before_reset = 1): same shapes, distributions and seed
+    "C3L1": dict(
+        spec=LayerSpec("GRU", seq=128, batch=8, input=512, hidden=512, direction="bidirectional",
+                       dtype="f16", init_h=True, lens=True, linear_before_reset=1, outputs=("Y", "Y_h")),
+        dists=Dists(W=("U", -0.044, 0.044), R=("U", -0.044, 0.044), B=("U", -0.1, 0.1),
+                    initial_h=("N", 0.0, 1.0), sequence_lens=("I", 1, 128)),
+        seed=3,
+        name="biGRU S128 B8 I512 H512 f16 L0 lens linear_before_reset"),
     "C4": dict(
         spec=LayerSpec("LSTM", seq=256, batch=64, input=1024, hidden=1024, layout=1, dtype="f16",
                        clip=3.0, input_forget=1, bias=False, peephole=True, lens=True,
