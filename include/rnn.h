@@ -28,6 +28,23 @@
  *   - Errors: a non-zero rnn_status; rnn_last_error() then returns a message
  *     naming the cell (LSTM, GRU or RNN) and the offending argument.  When any
  *     check fails, nothing has been enqueued.
+ *   - Environment switches, for tests and tuning (unset is the default;
+ *     each is read when a layer is planned or enqueued, and each keeps the
+ *     results within the layer's tolerance):
+ *       RNN_COOPERATIVE_LAUNCH=1    persistent kernels through the cooperative
+ *                                   launch API (bit-identical results)
+ *       RNN_PERSISTENT_UNITS=u      hidden units per workgroup of the
+ *                                   persistent engine
+ *       RNN_PERSISTENT_FALLBACK=k   force the persistent kernels' fallback of
+ *                                   one workgroup per direction on k workgroups
+ *       RNN_MFMA_RRES=0             stream R every step in the persistent
+ *                                   matrix-core step (bit-identical results)
+ *       RNN_MFMA_TILE=BMxUJ         force a matrix-core step tile
+ *       RNN_F32_SPLIT=0|1           f32 products on the f32 matrix cores (0)
+ *                                   or as three bf16 products (1, any size)
+ *       RNN_SMALL_PROJECTION=0|1    small-layer projection off or on
+ *       RNN_PROJ_LDS_MIN_TILES=n    tile count from which the 256x256
+ *                                   projection is taken
  */
 #ifndef ONNX_RNN_MI355X_H
 #define ONNX_RNN_MI355X_H

@@ -698,3 +698,51 @@ def test_streaming_continuation(cell, engine):
     assert torch.equal(y.view(torch.int32), rf["Y"].view(torch.int32)), f"{cell}: Y differs"
     for n in outs[1:]:
         assert torch.equal(rb[n].view(torch.int32), rf[n].view(torch.int32)), f"{cell}: {n} differs"
+
+
+# The persistent engine's units per workgroup, set with RNN_PERSISTENT_UNITS
+# (the tuning switch): every choice is the same layer, spread over a
+# different number of workgroups.
+UNITS = [("LSTM", "f32", 1, 40, (1, 3, 8)), ("GRU", "f16", 5, 72, (2, 12)), ("RNN", "f32", 8, 100, (1, 8))]
+
+
+@pytest.mark.parametrize("cell,dtype,B,H,units", UNITS, ids=[f"{c}-{d}-B{b}-H{h}" for c, d, b, h, _ in UNITS])
+def test_persistent_units_per_workgroup(cell, dtype, B, H, units, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=9, batch=B, input=24, hidden=H, direction="bidirectional", dtype=dtype,
+                     init_h=True, init_c=cell == "LSTM", lens=True, outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 83, Dists(sequence_lens=("I", 0, 9)))
+    blocks = set()
+    for u in units:
+        monkeypatch.setenv("RNN_PERSISTENT_UNITS", str(u))
+        layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+        assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+        blocks.add(layer.plan.step_blocks)
+        note(f"case persistent units {u} {cell} {dtype} B{B} H{H} blocks {layer.plan.step_blocks}")
+        check(spec, inp, engine="persistent", what=f"units {u} {cell} {dtype} B{B} H{H}")
+    assert len(blocks) == len(units), blocks       # each choice spreads the layer differently
+
+
+# Both persistent kernels launched with the cooperative API
+# (RNN_COOPERATIVE_LAUNCH = 1) instead of the plain launch with the
+# workgroups' own residency decision: the same kernels and arithmetic, so the
+# outputs are bit-identical to the plain launch and within the oracle's bar.
+COOP = [("LSTM", "f32", 1, 40), ("GRU", "f16", 3, 64), ("LSTM", "f16", 16, 64)]
+
+
+@pytest.mark.parametrize("cell,dtype,B,H", COOP, ids=[f"{c}-{d}-B{b}-H{h}" for c, d, b, h in COOP])
+def test_cooperative_launch(cell, dtype, B, H, monkeypatch):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=8, batch=B, input=24, hidden=H, direction="bidirectional", dtype=dtype,
+                     init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM",
+                     outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 89, Dists(sequence_lens=("I", 0, 8), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    layer = rl.Layer(spec, engine="persistent", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    plain = gpu_layer(spec, inp, engine="persistent")
+    monkeypatch.setenv("RNN_COOPERATIVE_LAUNCH", "1")
+    note(f"case cooperative launch {cell} {dtype} B{B} H{H}")
+    check(spec, inp, engine="persistent", what=f"cooperative {cell} {dtype} B{B} H{H}")
+    coop = gpu_layer(spec, inp, engine="persistent")
+    for n in plain:
+        assert np.array_equal(plain[n].view(np.uint8), coop[n].view(np.uint8)), f"{n}: cooperative launch differs"
