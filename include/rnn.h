@@ -140,7 +140,15 @@ typedef struct {
 
 /* Validate a description (64-bit checked arithmetic) and build the immutable
  * problem.  On success *out owns the problem; free it with
- * rnn_problem_destroy.  On error *out is set to NULL. */
+ * rnn_problem_destroy.  On error *out is set to NULL.
+ *
+ * Limits (RNN_ERR_UNSUPPORTED): hidden above 2^24; batch or seq above 2^30;
+ * engine = RNN_ENGINE_PERSISTENT on a shape that neither persistent form
+ * takes (batches of 9 to 15 never; the vector form needs a batch of at most
+ * 8 whose units fit the workgroups' LDS; the matrix-core form needs a batch
+ * of 16 or more whose tiles fit the chip at once).  RNN_ENGINE_AUTO never
+ * fails for that reason; rnn_problem_plan shows the engine it chose.  A
+ * tensor, Y or the projection scratch above 2^52 bytes is RNN_ERR_SHAPE. */
 int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** out);
 
 /* Free a problem (NULL is ignored). */

@@ -216,3 +216,37 @@ def test_validate_lengths(lib):
     assert e.value.code == rl.RNN_ERR_SHAPE and "sequence_lens[1]" in e.value.message
     with pytest.raises(rl.RnnError):
         rl.rnn_validate_lengths(np.array([-1]), 5)
+
+
+@pytest.mark.parametrize("cell,kw,needle", [
+    ("LSTM", dict(hidden=(1 << 24) + 1), "hidden: above"),
+    ("GRU", dict(batch=(1 << 30) + 1), "batch: above"),
+    ("RNN", dict(seq=(1 << 30) + 1), "seq: above"),
+])
+def test_create_unsupported_sizes(lib, cell, kw, needle):
+    rc, msg, h = create_err(rl.make_desc(spec(cell, **kw)))
+    assert rc == rl.RNN_ERR_UNSUPPORTED and needle in msg and msg.startswith(cell), (rc, msg)
+    assert h is None
+
+
+@pytest.mark.parametrize("cell,kw", [
+    ("LSTM", dict(hidden=1 << 24, seq=1, batch=1, input=1)),
+    ("GRU", dict(batch=1 << 30, seq=1, input=1, hidden=1)),
+    ("RNN", dict(seq=1 << 30, batch=1, input=1, hidden=1)),
+])
+def test_sizes_at_the_limits(lib, cell, kw):
+    h = rl.rnn_problem_create(rl.make_desc(spec(cell, **kw), "launch"))
+    xw, _ = rl.rnn_scratch_size(h)
+    G = {"LSTM": 4, "GRU": 3, "RNN": 1}[cell]
+    assert xw == 4 * kw["seq"] * kw["batch"] * G * kw["hidden"]
+    rl.rnn_problem_destroy(h)
+
+
+@pytest.mark.parametrize("kw", [dict(batch=9, hidden=40), dict(batch=15, hidden=40), dict(batch=3, hidden=5000),
+                                dict(batch=40, hidden=4000)])
+def test_persistent_engine_refuses_other_shapes(lib, kw):
+    rc, msg, _ = create_err(rl.make_desc(spec("LSTM", **kw), "persistent"))
+    assert rc == rl.RNN_ERR_UNSUPPORTED and "persistent engine" in msg, (rc, msg)
+    h = rl.rnn_problem_create(rl.make_desc(spec("LSTM", **kw), "auto"))   # the automatic choice takes it
+    assert rl.rnn_problem_plan(h).engine == rl.ENGINES["launch"]
+    rl.rnn_problem_destroy(h)
