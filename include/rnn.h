@@ -170,8 +170,12 @@ int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state
  * recurrent steps, which write whichever of Y, Y_h, Y_c is requested as they
  * go (the setup writes the outputs no step reaches).  Batch = 0 enqueues
  * nothing; Seq = 0 writes only Y_h / Y_c (initial states or zeros).  All
- * checks run before the first launch; on error nothing is enqueued.
- * sequence_lens is read on the device and not validated there. */
+ * checks run before the first launch; when one fails nothing is enqueued.
+ * RNN_ERR_HIP (the runtime refused a launch) may come after earlier stages
+ * were enqueued: the outputs are then undefined, and the scratch is in use
+ * until the stream has finished that work.  sequence_lens is read on the
+ * device and not validated there (rnn_validate_lengths checks it on the
+ * host). */
 int rnn_encode(const rnn_problem* problem, const rnn_operands* operands,
                void* xw_scratch, void* state_scratch, void* stream);
 
