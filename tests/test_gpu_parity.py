@@ -746,3 +746,24 @@ def test_cooperative_launch(cell, dtype, B, H, monkeypatch):
     coop = gpu_layer(spec, inp, engine="persistent")
     for n in plain:
         assert np.array_equal(plain[n].view(np.uint8), coop[n].view(np.uint8)), f"{n}: cooperative launch differs"
+
+
+# The largest hidden sizes the persistent engine takes (one more unit and the
+# automatic choice is one launch per step): every compute unit or nearly
+# every one holds a slice of R, and the layer is still exact.
+LARGEST = [("LSTM", "f32", 1, 1088), ("LSTM", "f16", 8, 1024), ("GRU", "f32", 4, 1184), ("RNN", "f32", 1, 2176)]
+
+
+@pytest.mark.parametrize("cell,dtype,B,H", LARGEST, ids=[f"{c}-{d}-B{b}-H{h}" for c, d, b, h in LARGEST])
+def test_persistent_largest_shapes(cell, dtype, B, H):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=6, batch=B, input=40, hidden=H, direction="bidirectional", dtype=dtype,
+                     init_h=True, init_c=cell == "LSTM", lens=B > 1, outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="auto", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    bigger = rl.Layer(spec.replace(hidden=H + 1), engine="auto", device="cuda:0")
+    assert bigger.plan.engine == rl.ENGINES["launch"]
+    s = 1.0 / np.sqrt(H)
+    inp = make_inputs(spec, 97, Dists(W=("U", -s, s), R=("U", -s, s), sequence_lens=("I", 1, 6)))
+    note(f"case persistent largest {cell} {dtype} B{B} H{H} blocks {layer.plan.step_blocks}")
+    check(spec, inp, engine="auto", what=f"largest persistent {cell} {dtype} B{B} H{H}")
