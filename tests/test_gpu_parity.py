@@ -767,3 +767,25 @@ def test_persistent_largest_shapes(cell, dtype, B, H):
     inp = make_inputs(spec, 97, Dists(W=("U", -s, s), R=("U", -s, s), sequence_lens=("I", 1, 6)))
     note(f"case persistent largest {cell} {dtype} B{B} H{H} blocks {layer.plan.step_blocks}")
     check(spec, inp, engine="auto", what=f"largest persistent {cell} {dtype} B{B} H{H}")
+
+
+# The persistent matrix-core step at its largest sizes (batches of 16 and
+# more, f16): hidden 4096 with R streamed, and the last hidden size before
+# the automatic choice turns to one launch per step for a GRU of batch 32.
+MLARGEST = [("LSTM", 16, 4096, "forward", False), ("RNN", 16, 4096, "bidirectional", False),
+            ("GRU", 32, 1024, "bidirectional", True)]
+
+
+@pytest.mark.parametrize("cell,B,H,direction,edge", MLARGEST, ids=[f"{c}-B{b}-H{h}" for c, b, h, _, _ in MLARGEST])
+def test_persistent_matrix_step_largest_shapes(cell, B, H, direction, edge):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=3, batch=B, input=40, hidden=H, direction=direction, dtype="f16",
+                     init_h=True, init_c=cell == "LSTM", lens=True, outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="auto", device="cuda:0")
+    assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
+    if edge:
+        assert rl.Layer(spec.replace(hidden=H + 8), engine="auto", device="cuda:0").plan.engine == rl.ENGINES["launch"]
+    s = 1.0 / np.sqrt(H)
+    inp = make_inputs(spec, 101, Dists(W=("U", -s, s), R=("U", -s, s), sequence_lens=("I", 1, 3)))
+    note(f"case persistent matrix-core largest {cell} B{B} H{H} blocks {layer.plan.step_blocks}")
+    check(spec, inp, engine="auto", what=f"largest persistent matrix-core {cell} B{B} H{H}")
