@@ -70,6 +70,8 @@ def _load():
         lib.oracle_projection.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, dp, dp, dp]
         lib.oracle_activation.restype = ctypes.c_double
         lib.oracle_activation.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        lib.oracle_round_half.restype = ctypes.c_uint16
+        lib.oracle_round_half.argtypes = [ctypes.c_double]
         _lib = lib
     return _lib
 
@@ -89,6 +91,14 @@ def _ptr(a, ctype=ctypes.c_double):
 def activation(name: str, alpha: float, beta: float, x: float) -> float:
     """One activation of the ONNX list, in double."""
     return _load().oracle_activation(_ACTS[name], alpha, beta, float(x))
+
+
+def round_half(values):
+    """Bits (uint16) of the binary16 values nearest to `values`, ties to even:
+    how a Half output holds a result."""
+    lib = _load()
+    v = np.asarray(values, np.float64)
+    return np.array([lib.oracle_round_half(float(x)) for x in v.reshape(-1)], np.uint16).reshape(v.shape)
 
 
 def projection(A, Bt):

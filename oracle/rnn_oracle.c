@@ -108,6 +108,34 @@ void oracle_projection(int64_t M, int64_t N, int64_t K, const double* A, const d
     }
 }
 
+/* Bits of the IEEE binary16 value nearest to x, ties to even: how a Half
+ * output holds a result ("How a layer runs", item 4: the outputs are rounded
+ * to Half; "Tolerance and evidence": Half outputs rounded from float32
+ * state).  Written from the format's definition: 1 sign bit, 5 exponent bits
+ * (bias 15), 10 fraction bits; normal numbers in [2^-14, 65504], subnormals
+ * multiples of 2^-24; a magnitude of 65520 (65504 plus half its spacing) or
+ * more overflows to infinity.  rint rounds to nearest even in the default
+ * rounding mode, and every division below is by a power of two, so exact. */
+uint16_t oracle_round_half(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  const double a = fabs(x);
+  if (isnan(x)) return (uint16_t)(sign | 0x7E00u);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+  if (a < ldexp(1.0, -14)) {                        /* subnormal (or zero): spacing 2^-24 */
+    const double q = rint(a / ldexp(1.0, -24));     /* 0 .. 1024; 1024 is the smallest normal */
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int e2 = 0;
+  (void)frexp(a, &e2);                              /* a = m * 2^e2, m in [0.5, 1) */
+  int e = e2 - 1;                                   /* a in [2^e, 2^(e+1)) */
+  double q = rint(a / ldexp(1.0, e - 10));          /* significand in units of the spacing: 1024 .. 2048 */
+  if (q == 2048.0) {
+    q = 1024.0;
+    e += 1;
+  }
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
 static double dot(const double* a, const double* b, int64_t n) {
   double s = 0.0;
   for (int64_t k = 0; k < n; ++k) s += a[k] * b[k];

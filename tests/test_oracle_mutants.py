@@ -46,6 +46,14 @@ MUTANTS = [
     ("Y zero past len dropped", "for (int64_t j = 0; j < H; ++j) y[j] = 0.0;", ""),
     ("bias Wb/Rb added twice Wb", "(Rb ? Rb[n] : 0.0);\n        }", "(Wb ? Wb[n] : 0.0);\n        }"),
     ("clip bound sign", "if (x < -clip) return -clip;", "if (x < -clip) return clip;"),
+    ("max_length ignored", "if (p->max_length > 0 && L > p->max_length) L = p->max_length;", ""),
+    ("max_length only with lengths", "if (p->max_length > 0 && L > p->max_length) L = p->max_length;",
+     "if (lens && p->max_length > 0 && L > p->max_length) L = p->max_length;"),
+    ("half ties away from zero", "const double q = rint(a / ldexp(1.0, -24));",
+     "const double q = round(a / ldexp(1.0, -24));"),
+    ("half normal ties away", "double q = rint(a / ldexp(1.0, e - 10));", "double q = round(a / ldexp(1.0, e - 10));"),
+    ("half overflow at the largest value", "if (a >= 65520.0)", "if (a > 65504.0)"),
+    ("half truncates", "double q = rint(a / ldexp(1.0, e - 10));", "double q = floor(a / ldexp(1.0, e - 10));"),
 ]
 
 
@@ -70,15 +78,52 @@ def test_planted_mistake_is_caught(name, old, new):
         lib.oracle_projection.argtypes = saved.oracle_projection.argtypes
         lib.oracle_activation.restype = saved.oracle_activation.restype
         lib.oracle_activation.argtypes = saved.oracle_activation.argtypes
+        lib.oracle_round_half.restype = saved.oracle_round_half.restype
+        lib.oracle_round_half.argtypes = saved.oracle_round_half.argtypes
         oracle._lib = lib
         try:
             caught = None
-            for pin_name, check in pins.all_pins(oracle.run):
+            for pin_name, check in pins.all_pins(oracle.run, oracle.round_half):
                 try:
                     check()
                 except AssertionError:
                     caught = pin_name
                     break
             assert caught is not None, f"no pin caught the planted mistake {name!r}"
+        finally:
+            oracle._lib = saved
+
+
+BRUTE_MUTANTS = [m for m in MUTANTS if not m[0].startswith("half ")]
+
+
+@pytest.mark.parametrize("name,old,new", BRUTE_MUTANTS, ids=[m[0] for m in BRUTE_MUTANTS])
+def test_brute_force_alone_catches_planted_mistake(name, old, new):
+    """The 50-digit brute force is a pin of its own: each planted mistake in
+    the layer arithmetic makes at least one brute-force case fail."""
+    from tests import test_oracle_brute as brute
+    saved = oracle._load()
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(tmp, name, old, new)
+        lib = ctypes.CDLL(so)
+        lib.oracle_rnn.restype = saved.oracle_rnn.restype
+        lib.oracle_rnn.argtypes = saved.oracle_rnn.argtypes
+        oracle._lib = lib
+        try:
+            caught = None
+            for case in brute.CASES:
+                try:
+                    brute.test_oracle_matches_brute_force(*case)
+                except AssertionError:
+                    caught = case[0]
+                    break
+            if caught is None:
+                for cell in ("RNN", "GRU", "LSTM"):
+                    try:
+                        brute.test_edge_lengths_and_max_length_brute_force(cell)
+                    except AssertionError:
+                        caught = f"edges {cell}"
+                        break
+            assert caught is not None, f"the brute force missed the planted mistake {name!r}"
         finally:
             oracle._lib = saved

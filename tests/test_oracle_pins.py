@@ -8,7 +8,7 @@ from oracle import oracle
 from tests import oracle_pins_lib as pins
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-CASES = pins.all_pins(oracle.run)
+CASES = pins.all_pins(oracle.run, oracle.round_half)
 
 
 @pytest.mark.parametrize("name,check", CASES, ids=[c[0] for c in CASES])
