@@ -35,8 +35,9 @@
  *                                   launch API (bit-identical results)
  *       RNN_PERSISTENT_UNITS=u      hidden units per workgroup of the
  *                                   persistent engine
- *       RNN_PERSISTENT_FALLBACK=k   force the persistent kernels' fallback of
- *                                   one workgroup per direction on k workgroups
+ *       RNN_PERSISTENT_FALLBACK=k   force the persistent kernels' fallback: k
+ *                                   workgroups take the place of the whole
+ *                                   grid in turn (bit-identical results)
  *       RNN_MFMA_RRES=0             stream R every step in the persistent
  *                                   matrix-core step (bit-identical results)
  *       RNN_MFMA_TILE=BMxUJ         force a matrix-core step tile
@@ -202,6 +203,34 @@ typedef struct {
   int32_t step_launches;   /* launches of the recurrent-step stage per rnn_encode */
 } rnn_plan_info;
 int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info);
+
+/* What the recurrent-step stage of the last rnn_encode on this state scratch
+ * did, read back from the status words a persistent step kernel leaves in the
+ * state scratch ("Recurrent layers" page, "How a layer runs", item 3: the
+ * steps; here they may run in one launch whose workgroups wait on one
+ * another).  Enqueues a copy of those words on `stream` (a hipStream_t; NULL
+ * is the default stream) and waits for the stream, so it returns after every
+ * call enqueued there before it has finished.
+ *   persistent          1 when a persistent step kernel ran, else 0 (and the
+ *                       fields below are 0)
+ *   fallback_workgroups 0: every workgroup of the grid ran at once (the fast
+ *                       path); k > 0: the device did not hold the whole grid
+ *                       at once (say, it was partly busy with other work) and
+ *                       k workgroups took the place of the others in turn.
+ *                       The outputs are bit-identical either way; the
+ *                       fallback is slower.
+ *   timed_out           1: a wait between workgroups passed its safety bound
+ *                       (several seconds) and the kernel ended early: the
+ *                       outputs are incomplete
+ * Errors: RNN_ERR_ARG for a NULL argument (state_scratch may be NULL only
+ * when rnn_scratch_size reports 0 state bytes), RNN_ERR_HIP when the copy
+ * fails.  The state scratch is owned by the caller and only read. */
+typedef struct {
+  int32_t persistent;
+  int32_t fallback_workgroups;
+  int32_t timed_out;
+} rnn_run_status;
+int rnn_read_run_status(const rnn_problem* problem, const void* state_scratch, void* stream, rnn_run_status* out);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* rnn_last_error(void);

@@ -59,6 +59,11 @@ class rnn_operands(ctypes.Structure):
     _fields_ = [(n, rnn_tensor) for n in OPERAND_NAMES]
 
 
+class rnn_run_status(ctypes.Structure):
+    _fields_ = [("persistent", ctypes.c_int32), ("fallback_workgroups", ctypes.c_int32),
+                ("timed_out", ctypes.c_int32)]
+
+
 class rnn_plan_info(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("steps", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("step_blocks", ctypes.c_int32), ("step_launches", ctypes.c_int32)]
@@ -97,6 +102,8 @@ def load_library(path: str = LIB_PATH):
     lib.rnn_validate_lengths.restype = ctypes.c_int
     lib.rnn_problem_plan.argtypes = [ctypes.c_void_p, P(rnn_plan_info)]
     lib.rnn_problem_plan.restype = ctypes.c_int
+    lib.rnn_read_run_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P(rnn_run_status)]
+    lib.rnn_read_run_status.restype = ctypes.c_int
     lib.rnn_last_error.argtypes = []
     lib.rnn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -166,6 +173,13 @@ def rnn_problem_plan(handle) -> rnn_plan_info:
     return info
 
 
+def rnn_read_run_status(handle, state_scratch_ptr: int, stream_ptr: int = 0) -> rnn_run_status:
+    out = rnn_run_status()
+    _check(load_library().rnn_read_run_status(handle, ctypes.c_void_p(state_scratch_ptr or None),
+                                              ctypes.c_void_p(stream_ptr or None), ctypes.byref(out)))
+    return out
+
+
 def rnn_validate_lengths(lens, seq: int) -> int:
     import numpy as np
     arr = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
@@ -228,6 +242,12 @@ class Layer:
             rnn_encode(self.handle, ops, xw, self.state.data_ptr(), st.cuda_stream)
         else:
             rnn_encode_timed(self.handle, ops, xw, self.state.data_ptr(), st.cuda_stream, events)
+
+    def run_status(self, stream=None) -> rnn_run_status:
+        """rnn_read_run_status of this layer's state scratch (waits for the stream)."""
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return rnn_read_run_status(self.handle, self.state.data_ptr() if self.state_bytes else 0, st.cuda_stream)
 
     def __del__(self):
         try:

@@ -150,6 +150,11 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   p->xw_bytes = (p->S > 0 && p->B > 0) ? size_t(xw) : 0;
   int64_t dbh;
   if (!mul3(p->D, p->B, p->H, &dbh) || dbh > kMaxBytes / 8) return bad(RNN_ERR_SHAPE, "state: size overflows");
+  // The matrix-core step's tile, once: every launch of this problem uses it
+  // (RNN_MFMA_TILE is read here only).
+  if (mfma_step_supported(*p))
+    mfma_tile(int(p->B), int(p->H), p->D, p->G - ((cell == RNN_CELL_LSTM && desc->input_forget) ? 1 : 0),
+              &p->mfma_bm, &p->mfma_uj);
   // Engine choice.
   int blocks = 0, units = 0, wpd = 0;
   const bool pers_ok = persistent_supported(*p, &blocks, &units, &wpd);
@@ -222,12 +227,12 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     st.xch = off;   off = align256(off + 2 * size_t(dbh) * 8);
     st.xch2 = off;  off = align256(off + (cell == RNN_CELL_GRU && !desc->linear_before_reset ? 2 * size_t(dbh) * 8 : 0));
     st.status = off; off = align256(off + 3 * 4);   // status, arrival tickets, residency decision
-    // the per-step engine's state, for the fallback taken when the grid does
-    // not run all at once
-    st.hbuf = off;  off = align256(off + 2 * size_t(dbh) * 4);
+    // what the fallback (taken when the grid does not run all at once) keeps
+    // in memory where the fast path keeps registers: the cell state and a
+    // GRU's z between its two phases.  No h slots: h travels in the words.
     st.cell = off;  off = align256(off + size_t(dbh) * 4);
     st.zbuf = off;  off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
-    st.rhbuf = off; off = align256(off + (cell == RNN_CELL_GRU ? size_t(dbh) * 4 : 0));
+    st.hbuf = st.rhbuf = SIZE_MAX;
   } else {
     st.hbuf = off;  off = align256(off + 2 * size_t(dbh) * 4);
     st.cell = off;  off = align256(off + size_t(dbh) * 4);
@@ -242,7 +247,7 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     }
     if (p->pers_mfma) {
       st.flags = off;   off = align256(off + size_t(kPersistentMfmaTiles) * 4);
-      st.status = off;  off = align256(off + 4);
+      st.status = off;  off = align256(off + 3 * 4);   // status, arrival tickets, residency decision
     }
   }
   st.total = p->B > 0 ? off : 0;
@@ -303,6 +308,30 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
   }
   info->launches = n;
   info->step_launches = (p->B > 0 && p->S > 0) ? step_launch_count(*p) : 0;
+  return RNN_OK;
+}
+
+extern "C" int rnn_read_run_status(const rnn_problem* problem, const void* state_scratch, void* stream,
+                                   rnn_run_status* out) {
+  g_error.clear();
+  if (!problem || !out) return fail(RNN_ERR_ARG, -1, "problem/out: NULL");
+  const Problem& p = *reinterpret_cast<const Problem*>(problem);
+  *out = rnn_run_status{0, 0, 0};
+  if (p.engine != RNN_ENGINE_PERSISTENT || p.st.total == 0) return RNN_OK;
+  if (!state_scratch) return fail(RNN_ERR_ARG, p.desc.cell, "state_scratch: NULL");
+  // status (1: a wait passed its bound), arrival tickets, residency decision
+  // (0: no kernel ran, 1: every workgroup at once, 2 | k << 8: k workgroups
+  // ran the fallback)
+  int words[3] = {0, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(words, static_cast<const char*>(state_scratch) + p.st.status, sizeof words,
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(RNN_ERR_HIP, p.desc.cell, "status read: %s", hipGetErrorString(e));
+  if (words[2] == 0) return RNN_OK;
+  out->persistent = 1;
+  out->fallback_workgroups = words[2] == 1 ? 0 : (words[2] >> 8);
+  out->timed_out = words[0] != 0;
   return RNN_OK;
 }
 
@@ -384,7 +413,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* st = static_cast<char*>(state_scratch);
   const bool pers = p.engine == RNN_ENGINE_PERSISTENT && !p.pers_mfma;   // the small-batch persistent engine
-  float* hbuf = reinterpret_cast<float*>(st + p.st.hbuf);
+  float* hbuf = p.st.hbuf == SIZE_MAX ? nullptr : reinterpret_cast<float*>(st + p.st.hbuf);
   float* cstate = reinterpret_cast<float*>(st + p.st.cell);
   int* status = (pers || p.pers_mfma) ? reinterpret_cast<int*>(st + p.st.status) : nullptr;
   int* flags = p.pers_mfma ? reinterpret_cast<int*>(st + p.st.flags) : nullptr;
@@ -445,7 +474,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   a.layout = p.desc.layout;
   a.cell_state = cstate;
   a.zbuf = reinterpret_cast<float*>(st + p.st.zbuf);
-  a.rhbuf = reinterpret_cast<float*>(st + p.st.rhbuf);
+  a.rhbuf = p.st.rhbuf == SIZE_MAX ? nullptr : reinterpret_cast<float*>(st + p.st.rhbuf);
   a.xch = reinterpret_cast<unsigned long long*>(st + p.st.xch);
   a.xch2 = reinterpret_cast<unsigned long long*>(st + p.st.xch2);
   a.clip = p.desc.clip > 0.f ? p.desc.clip : 0.f;

@@ -491,10 +491,8 @@ static MfmaStepArgs phase_args(const StepArgs& a, const Problem& p, int step, in
     m.gate_of[gi++] = g;
   }
   m.Gp = gi;
-  int uj = 16;
-  *bm = 16;
-  mfma_tile(a.B, a.H, a.D, p.G - (skip_f ? 1 : 0), bm, &uj);
-  m.UJ = uj;
+  *bm = p.mfma_bm;
+  m.UJ = p.mfma_uj;
   return m;
 }
 
@@ -545,9 +543,7 @@ bool mfma_persistent_supported(const Problem& p, int* tiles_out) {
   t.H = int(p.H);
   t.B = int(p.B);
   if (!step_dma_supported(t, mode)) return false;
-  const bool skip_f = p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget;
-  int bm = 16, uj = 16;
-  mfma_tile(int(p.B), int(p.H), p.D, p.G - (skip_f ? 1 : 0), &bm, &uj);
+  const int bm = p.mfma_bm, uj = p.mfma_uj;
   const int64_t tiles = ((p.H + uj - 1) / uj) * ((p.B + bm - 1) / bm) * p.D;
   if (tiles > kPersistentMfmaTiles) return false;
   *tiles_out = int(tiles);

@@ -464,12 +464,15 @@ __device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& fi
   }
 }
 
-// One step (one phase of a two-phase GRU step) of one tile, run by a
-// per-step launch (PERS = false) or inside the persistent kernel below.  RR:
-// the tile's R rows stay in LDS for the whole layer (loaded at step 0; the
-// persistent form in f16 mode with one phase per step only).
+// One step (one phase of a two-phase GRU step) of tile (tx, ty, tz): units
+// tx*UJ.., batch rows ty*BM.., direction tz.  Run by a per-step launch (PERS =
+// false) or inside the persistent kernel below (each workgroup its own tile;
+// in the fallback one workgroup every tile of a group in turn).  RR: the
+// tile's R rows stay in LDS for the whole layer (loaded at step 0, or at
+// every call when `reload_r`; the persistent form in f16 mode with one phase
+// per step only).
 template <int MODE, int BM, int CB, bool PERS, bool RR = false>
-__device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
+__device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, int ty, int tz, bool reload_r = false) {
   static_assert(!RR || (PERS && MODE == 1), "resident R: persistent form, f16 mode");
   typedef DmaCfg<MODE, BM, CB, RR> C;
   typedef typename C::Geo Geo;
@@ -491,9 +494,9 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   const StepArgs& a = m.a;
   const int H = a.H, B = a.B, G = a.G, S = a.S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j0 = blockIdx.x * m.UJ;
-  const int b0 = blockIdx.y * BM;
-  const int d = blockIdx.z;
+  const int j0 = tx * m.UJ;
+  const int b0 = ty * BM;
+  const int d = tz;
   const int UJ = m.UJ, ncb = (m.Gp * UJ) >> 4;
   const int ujs = __builtin_ctz(unsigned(UJ));   // UJ is a power of two
 
@@ -597,7 +600,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
   // the layout of a chunk's R part; loaded before the first chunks, so the
   // chunk waits (the counter retires in order) cover it
   if constexpr (RR) {
-    if (s == 0) {
+    if (s == 0 || reload_r) {
       for (int kc = 0; kc < nk; ++kc)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -794,7 +797,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s) {
 
 template <int MODE, int BM, int CB>
 __global__ __launch_bounds__(kMThreads) void step_dma_kernel(MfmaStepArgs m) {
-  dma_step<MODE, BM, CB, false>(m, m.step);
+  dma_step<MODE, BM, CB, false>(m, m.step, int(blockIdx.x), int(blockIdx.y), int(blockIdx.z));
 }
 
 // Every step in one launch (all tiles resident together, settled as in
@@ -819,8 +822,8 @@ constexpr long kFlagSpinLimit = 1l << 22;
 
 template <int MODE, int BM, int CB, bool RR>
 __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p) {
-  // launched plainly: every workgroup running (GO), or one workgroup per
-  // direction runs the layer on the per-step engine's state (residency.h)
+  // launched plainly: every workgroup running (GO), or the workgroups that
+  // arrived run every tile in turn (below; residency.h)
   __shared__ int coop_dec, coop_ticket;
   if (threadIdx.x == 0) {
     const int t = arrive_ticket(p.status + 1);
@@ -828,13 +831,27 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
     coop_ticket = t;
   }
   __syncthreads();
+  const int steps = p.ph[0].a.steps, P = p.P;
   if (__builtin_expect(coop_dec != 1, 0)) {
-    // the tensors' element type: f16 in mode 1, f32 in modes 0 and 2 (the
-    // launcher refuses any other pairing)
-    typedef typename std::conditional<MODE == 1, half_t, float>::type T;
+    // Fallback: the tiles of one batch tile and direction depend only on one
+    // another, so the workgroups that arrived take such groups (group g =
+    // batch tile + tiles_y * direction, the ticket's groups g = ticket,
+    // ticket + count, ...) and run every tile of a group in turn, step by
+    // step and phase by phase, through the same tile body as the fast path:
+    // the results are bit-identical.  One workgroup's own stores are complete
+    // (and so visible to its later loads) after each tile's final wait.
     const int cnt = coop_dec >> 8;
-    if (coop_ticket < cnt)
-      for (int dd = coop_ticket; dd < p.ph[0].a.D; dd += cnt) fallback_direction<T>(p.ph[0].a, dd);
+    const int gx = int(gridDim.x), gy = int(gridDim.y);
+    const int groups = gy * int(gridDim.z);
+    for (int g = coop_ticket; coop_ticket < cnt && g < groups; g += cnt)
+      for (int s = 0; s < steps; ++s)
+        for (int ph = 0; ph < P; ++ph)
+          for (int x = 0; x < gx; ++x) {
+            if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s, x, g % gy, g / gy, true);
+            else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s, x, g % gy, g / gy, true);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            __syncthreads();
+          }
     return;
   }
   __shared__ int abort_s;
@@ -842,7 +859,6 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
   const int row = int(blockIdx.y + gridDim.y * blockIdx.z);   // batch tile and direction
   const int me = int(blockIdx.x) + gx * row;
   const int* peers = p.flags + gx * row;
-  const int steps = p.ph[0].a.steps, P = p.P;
   if (threadIdx.x == 0) abort_s = 0;
   __syncthreads();
   for (int s = 0; s < steps; ++s)
@@ -865,8 +881,8 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
           return;
         }
       }
-      if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s);
-      else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s);
+      if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s, int(blockIdx.x), int(blockIdx.y), int(blockIdx.z));
+      else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s, int(blockIdx.x), int(blockIdx.y), int(blockIdx.z));
       // every state store of this workgroup has completed before the flag
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
       __syncthreads();

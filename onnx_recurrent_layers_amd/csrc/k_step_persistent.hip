@@ -448,6 +448,211 @@ constexpr bool mfma_products() {
   return sizeof(T) == 2 && DEF && NB >= 4;
 }
 
+// The R rows of the units u0 .. u0+Uw-1 of direction d (every computed gate
+// block) into LDS: row gi*U + uu holds R[d][gate_of[gi]*H + u0 + uu][0..H),
+// zero past H up to H4 and for uu >= Uw.
+template <typename T>
+__device__ __forceinline__ void load_rows(const PersArgs& p, T* Rl, int RS, int d, int u0, int Uw, int H4) {
+  const int H = p.a.H;
+  const T* Rd = static_cast<const T*>(p.a.R) + int64_t(d) * p.a.G * H * H;
+  for (int e = threadIdx.x; e < p.NR * H4; e += kPThreads) {
+    const int r = e / H4, k = e - r * H4;
+    const int gi = r / p.U, uu = r - gi * p.U;
+    Rl[r * RS + k] = (uu < Uw && k < H) ? Rd[int64_t(p.gate_of[gi] * H + u0 + uu) * H + k] : T(0.f);
+  }
+}
+
+// Gate arithmetic of one (unit, batch row) element in the step's first (or
+// only) phase, in the order of cells.h.  Shared by the fast path and the
+// fallback, so that both take exactly the same operations.  rec_of(gi) is
+// the recurrent sum of computed gate block gi; xv, wb, rb hold the
+// projection and biases of gate block g at index g.  Returns the new h
+// (LSTM, RNN, GRU with linear_before_reset = 1; c is updated in place); for
+// a GRU with linear_before_reset = 0 (cand >= 0) it leaves z and r*h for the
+// second phase and returns 0.
+template <bool DEF, typename RecOf>
+__device__ __forceinline__ float gates_first(const StepArgs& a, int cand, const Act* acts, const float* xv,
+                                             RecOf rec_of, const float* wb, const float* rb, const float* peep,
+                                             float& c, float hown, float& z, float& rh) {
+  auto pre = [&](int gi, int g) { return pre_sum(xv[g], rec_of(gi), wb[g], rb[g]); };
+  float hnew = 0.f;
+  if (a.cell == RNN_CELL_LSTM) {
+    float p4[4];
+    p4[0] = pre(0, 0);
+    p4[1] = pre(1, 1);
+    if (a.input_forget) {
+      p4[2] = 0.f;
+      p4[3] = pre(2, 3);
+    } else {
+      p4[2] = pre(2, 2);
+      p4[3] = pre(3, 3);
+    }
+    lstm_unit<DEF>(p4, a.P ? peep : nullptr, c, a.clip, a.input_forget, acts, &hnew, &c);
+  } else if (a.cell == RNN_CELL_GRU) {
+    z = gru_gate<DEF>(pre(0, 0), a.clip, acts);
+    const float r = gru_gate<DEF>(pre(1, 1), a.clip, acts);
+    if (cand < 0) {
+      // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+      const float ph = (xv[2] + r * (rec_of(2) + rb[2])) + wb[2];
+      hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
+    } else {
+      rh = r * hown;
+    }
+  } else {
+    hnew = rnn_unit<DEF>(pre(0, 0), a.clip, acts);
+  }
+  return hnew;
+}
+
+// Second phase of a GRU step with linear_before_reset = 0:
+// h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h), h = (1 - z)*h~ + z*h.
+template <bool DEF>
+__device__ __forceinline__ float gates_cand(const StepArgs& a, const Act* acts, float xw_h, float rec_h, float wb_h,
+                                            float rb_h, float z, float hown) {
+  const float ph = pre_sum(xw_h, rec_h, wb_h, rb_h);
+  return gru_unit<DEF>(z, ph, hown, a.clip, acts);
+}
+
+// The layer's direction d by one workgroup alone, for the fallback of the
+// residency decision (not every workgroup of the grid is running, so none may
+// wait on another).  The workgroup takes the place of each workgroup of the
+// direction in turn, every step: it loads that workgroup's R rows into the
+// same LDS layout, stages the same exchange words (already published, so the
+// polls return at once), runs the same products and the same gate code, and
+// publishes the same words.  Every result is therefore bit-identical to the
+// fast path.  What the fast path keeps in registers across steps comes from
+// memory instead: the cell state (cell_state, initialised by the state
+// setup), the own h (the exchange word the unit published, or step 0's word
+// from the setup) and a GRU's z between its two phases (zbuf).  Returns
+// non-zero when a wait ran past its safety bound.
+template <typename T, int NB, bool DEF>
+__device__ __forceinline__ int fallback_blocks(const PersArgs& p, int d, unsigned char* smem) {
+  const StepArgs& a = p.a;
+  const int H = a.H, B = a.B, S = a.S, G = a.G;
+  const int tid = threadIdx.x;
+  const int64_t DBH = int64_t(a.D) * B * H;
+  const int64_t dBH = int64_t(d) * B * H;
+  const int GH = G * H;
+  const int H4 = (H + 31) & ~31;
+  const int RS = H4 + 8;
+  constexpr bool MF = mfma_products<T, NB, DEF>();
+  const int HS = H4 + 8;
+  T* Rl = reinterpret_cast<T*>(smem);
+  const size_t r_bytes = (size_t(p.NR) * RS * sizeof(T) + 15) & ~size_t(15);
+  void* hs = smem + r_bytes;
+  float* rec = reinterpret_cast<float*>(smem + r_bytes + (MF ? size_t(4) * NB * HS : size_t(4) * NB * H4));
+  const int NRNB = p.NR * NB;
+  const bool ksplit = !MF && p.NR <= 16 && H4 >= 64;
+  auto recv = [&](int r, int b) {
+    const int i = r * NB + b;
+    if constexpr (MF) return ((rec[i] + rec[NRNB + i]) + rec[2 * NRNB + i]) + rec[3 * NRNB + i];
+    else return ksplit ? rec[i] + rec[NRNB + i] : rec[i];
+  };
+  auto run_products = [&](int r_lo, int r_hi) {
+    if constexpr (MF)
+      products_mfma<NB>(reinterpret_cast<const half_t*>(Rl), RS, static_cast<const half_t*>(hs), HS, rec, r_lo, r_hi,
+                        p.NR, H4);
+    else if (ksplit)
+      products_ksplit<T, NB>(Rl, RS, static_cast<const float*>(hs), rec, NRNB, r_lo, r_hi, H4);
+    else
+      products<T, NB>(Rl, RS, static_cast<const float*>(hs), rec, r_lo, r_hi, H4);
+  };
+  if constexpr (MF) {
+    for (int e = tid; e < 2 * NB * HS; e += kPThreads) static_cast<half_t*>(hs)[e] = half_t(0.f);
+  } else {
+    for (int e = NB * H + tid; e < NB * H4; e += kPThreads) static_cast<float*>(hs)[e] = 0.f;
+  }
+  int maxL = 0;
+  unsigned lens_left[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    lens_left[b] = b < B ? unsigned(row_length(a.lens, b, S, a.steps)) : 0u;
+    maxL = max(maxL, int(lens_left[b]));
+  }
+  const int g_uu = tid / NB, g_b = tid % NB;
+  int L = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (g_b == b) L = int(lens_left[b]);
+  const Act* acts = a.act + d * a.slots;
+  const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
+  const bool rev = a.dir_reverse[d] != 0;
+  const bool poller = tid >= kPThreads - kPollThreads;
+  const int ptid = tid - (kPThreads - kPollThreads);
+  WordMap wmap;
+  if (poller) map_words<NB, MF>(wmap, ptid, H, HS);
+  const int phases = p.cand >= 0 ? 2 : 1;
+  const int nrows_main = p.cand >= 0 ? p.cand * p.U : p.NR;
+  __shared__ int fb_fail;
+  if (tid == 0) fb_fail = 0;
+  for (int s = 0; s < maxL; ++s) {
+    unsigned amask = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) amask |= (unsigned(s) < lens_left[b] ? 1u : 0u) << b;
+    for (int ph = 0; ph < phases; ++ph)
+      for (int vb = 0; vb < p.WPD; ++vb) {
+        const int u0 = vb * p.U;
+        const int Uw = min(p.U, H - u0);
+        __syncthreads();   // the previous block is done with the LDS
+        load_rows<T>(p, Rl, RS, d, u0, Uw, H4);
+        if (poller) {
+          const unsigned long long* src = (ph == 0 ? a.xch : a.xch2) + (s & 1) * DBH + dBH;
+          if (stage_words<NB, MF>(src, hs, unsigned(s), H, HS, amask, wmap, ptid)) fb_fail = 1;
+        }
+        __syncthreads();
+        if (fb_fail) return 1;
+        run_products(ph == 0 ? 0 : nrows_main, ph == 0 ? nrows_main : p.NR);
+        __syncthreads();
+        const int j = u0 + g_uu;
+        if (!(g_uu < Uw && g_b < B && s < L)) continue;
+        const int64_t si = dBH + int64_t(g_b) * H + j;
+        const int t = rev ? L - 1 - s : s;
+        const float* xw = a.xw + ((int64_t(d) * S + t) * B + g_b) * GH + j;
+        float xv[4] = {0.f, 0.f, 0.f, 0.f}, wb[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
+        float peep[3] = {0.f, 0.f, 0.f};
+        for (int g = 0; g < G; ++g) {
+          if (!(a.input_forget && g == 2)) xv[g] = xw[g * H];
+          if (bias) {
+            wb[g] = ld(bias, g * H + j);
+            rb[g] = ld(bias, GH + g * H + j);
+          }
+        }
+        if (a.P) {
+          const T* P = static_cast<const T*>(a.P) + int64_t(d) * 3 * H;
+          peep[0] = ld(P, j);
+          peep[1] = ld(P, H + j);
+          peep[2] = ld(P, 2 * H + j);
+        }
+        const float hown = __uint_as_float(static_cast<unsigned>(load_word(a.xch + (s & 1) * DBH + si)));
+        float hnew, c = 0.f;
+        if (ph == 0) {
+          float z = 0.f, rh = 0.f;
+          if (a.cell == RNN_CELL_LSTM) c = a.cell_state[si];
+          hnew = gates_first<DEF>(a, p.cand, acts, xv, [&](int gi) { return recv(gi * p.U + g_uu, g_b); }, wb, rb,
+                                  peep, c, hown, z, rh);
+          if (a.cell == RNN_CELL_LSTM) a.cell_state[si] = c;
+          if (p.cand >= 0) {
+            a.zbuf[si] = z;
+            put_word(a.xch2 + (s & 1) * DBH + si, unsigned(s), rh);
+            continue;
+          }
+        } else {
+          hnew = gates_cand<DEF>(a, acts, xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2], a.zbuf[si], hown);
+        }
+        put_word(a.xch + ((s + 1) & 1) * DBH + si, unsigned(s + 1), hnew);
+        if (p.Y)
+          static_cast<T*>(p.Y)[y_index(p.layout, S, a.D, B, H, t, d, g_b, j)] = to_elem<T>(hnew);
+        if (s == L - 1) {
+          const int64_t oi = state_index(p.layout, a.D, B, H, d, g_b, j);
+          if (p.Y_h) static_cast<T*>(p.Y_h)[oi] = to_elem<T>(hnew);
+          if (p.Y_c) static_cast<T*>(p.Y_c)[oi] = to_elem<T>(c);
+        }
+      }
+  }
+  __syncthreads();
+  return 0;
+}
+
 template <typename T, int NB, bool DEF>
 __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -489,12 +694,7 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   };
 
   // R rows of this workgroup's units, resident for the whole layer
-  const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * GH * H;
-  for (int e = tid; e < p.NR * H4; e += kPThreads) {
-    const int r = e / H4, k = e - r * H4;
-    const int gi = r / p.U, uu = r - gi * p.U;
-    Rl[r * RS + k] = (uu < Uw && k < H) ? Rd[int64_t(p.gate_of[gi] * H + u0 + uu) * H + k] : T(0.f);
-  }
+  load_rows<T>(p, Rl, RS, d, u0, Uw, H4);
   // padded tail of h stays zero (the f16 planes are cleared whole: columns of
   // absent batch rows feed only dropped outputs, but must not hold Inf or NaN)
   if constexpr (MF) {
@@ -515,8 +715,10 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   // and cost C2 3 % per layer)
   if (__builtin_expect(coop_dec != 1, 0)) {
     const int cnt = coop_dec >> 8;
+    int fail = 0;
     if (coop_ticket < cnt)
-      for (int dd = coop_ticket; dd < a.D; dd += cnt) fallback_direction<T>(a, dd);
+      for (int dd = coop_ticket; dd < a.D && !fail; dd += cnt) fail = fallback_blocks<T, NB, DEF>(p, dd, smem);
+    if (fail && tid == 0) atomicExch(p.status, 1);
     return;
   }
 
@@ -646,32 +848,10 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     // 3. gate arithmetic
     float hnew = 0.f, z = 0.f;
     if (live) {
-      auto pre = [&](int gi, int g) { return pre_sum(xv[g], recv(gi * p.U + g_uu, g_b), wb[g], rb[g]); };
-      if (a.cell == RNN_CELL_LSTM) {
-        float p4[4];
-        p4[0] = pre(0, 0);
-        p4[1] = pre(1, 1);
-        if (a.input_forget) {
-          p4[2] = 0.f;
-          p4[3] = pre(2, 3);
-        } else {
-          p4[2] = pre(2, 2);
-          p4[3] = pre(3, 3);
-        }
-        lstm_unit<DEF>(p4, a.P ? peep : nullptr, c, a.clip, a.input_forget, acts, &hnew, &c);
-      } else if (a.cell == RNN_CELL_GRU) {
-        z = gru_gate<DEF>(pre(0, 0), a.clip, acts);
-        const float r = gru_gate<DEF>(pre(1, 1), a.clip, acts);
-        if (p.cand < 0) {
-          // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
-          const float ph = (xv[2] + r * (recv(2 * p.U + g_uu, g_b) + rb[2])) + wb[2];
-          hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
-        } else {
-          put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), r * hown);
-        }
-      } else {
-        hnew = rnn_unit<DEF>(pre(0, 0), a.clip, acts);
-      }
+      float rh = 0.f;
+      hnew = gates_first<DEF>(a, p.cand, acts, xv, [&](int gi) { return recv(gi * p.U + g_uu, g_b); }, wb, rb, peep,
+                              c, hown, z, rh);
+      if (p.cand >= 0) put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), rh);
     }
 
     if (p.cand >= 0) {
@@ -683,11 +863,7 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
       if ((abort_run = abort_flag) != 0) break;
       run_products(p.cand * p.U, p.NR);
       lds_barrier();
-      if (live) {
-        // h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
-        const float ph = pre_sum(xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2]);
-        hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
-      }
+      if (live) hnew = gates_cand<DEF>(a, acts, xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2], z, hown);
     }
 
     if (live) {

@@ -19,7 +19,9 @@ struct Act {
   float beta;
 };
 
-// Byte offsets of the regions inside the caller's state scratch.
+// Byte offsets of the regions inside the caller's state scratch (SIZE_MAX:
+// the layout has no such region; the small-batch persistent engine keeps h in
+// its exchange words and has no h slots nor r*h buffer).
 struct StateLayout {
   size_t hbuf;     // f32 h, two slots of [D][B][H]: slot s & 1 holds h of step s (slot 0 = initial h)
   size_t cell;     // f32 c: [D][B][H] (LSTM), updated in place, final after the last step
@@ -53,6 +55,9 @@ struct Problem {
   int pers_wg_per_dir = 0;
   // the persistent engine in its matrix-core form (batches of 16 and more)
   bool pers_mfma = false;
+  // tile of the matrix-core step (batch rows, units), fixed when the problem
+  // is created (batches of 16 and more)
+  int mfma_bm = 16, mfma_uj = 16;
   // f32 tensors: the projection on the bf16 matrix cores (three split
   // products) instead of the f32 matrix cores
   bool f32_split_proj = false;
@@ -118,10 +123,10 @@ struct SetupArgs {
   int dtype;
   const void* init_h;  // or null
   const void* init_c;  // or null
-  float* hbuf;         // slot 0 of the per-step engine's h (also the persistent engine's fallback), or null
+  float* hbuf;         // slot 0 of the per-step engines' h, or null
   unsigned short* hsplit;  // slot 0 of h as 16-bit hi and lo planes, or null
   int split_kind;          // 1 f16 halves, 2 bf16 halves
-  float* cell_state;   // or null (persistent engine)
+  float* cell_state;   // or null
   unsigned long long* xch;   // tagged h words [2][D][B][H], or null (per-step engine)
   unsigned long long* xch2;  // tagged r*h words [2][D][B][H], or null
   int* status;               // persistent engine status word and the two residency words after it, or null
@@ -153,6 +158,8 @@ hipError_t launch_step_generic(const StepArgs& a, int step, hipStream_t s);
 int step_generic_launches_per_step(const StepArgs& a);
 hipError_t launch_step_mfma(const StepArgs& a, const Problem& p, int step, hipStream_t s);
 bool mfma_step_supported(const Problem& p);
+// Tile of the matrix-core step for a problem (RNN_MFMA_TILE may force one).
+void mfma_tile(int B, int H, int D, int Gp, int* bm, int* uj);
 // Persistent form of the matrix-core step: one launch for every
 // step, at most kPersistentMfmaTiles workgroups (one per compute unit).
 constexpr int kPersistentMfmaTiles = 256;

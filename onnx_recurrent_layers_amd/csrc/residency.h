@@ -1,21 +1,22 @@
 // residency.h -- how a grid launched plainly settles whether all of its
-// workgroups run at once, and the one-workgroup-per-direction fallback taken
-// when they do not.  Used by the two persistent step kernels, whose
-// workgroups wait on one another.  HIP's cooperative launch guarantees
+// workgroups run at once.  Used by the two persistent step kernels, whose
+// workgroups wait on one another; each kernel has its own fallback for when
+// they do not (the workgroups that arrived take the place of the others in
+// turn, through the same arithmetic).  HIP's cooperative launch guarantees
 // co-residency but costs about 18 us per launch on this runtime; a plain
 // launch (after a host check that the grid fits the device) plus this
 // decision gives the same guarantee: GO only when every workgroup has taken
 // its ticket, i.e. is running.  Internal.
 #pragma once
 
-#include "step_wave.h"
+#include "cells.h"
 
 namespace rnnhip {
 
 // Residency decision, taken by thread 0 of every workgroup.  coop[0] counts
 // arrivals, coop[1] holds the decision: 1 (GO: every workgroup is running)
 // or 2 | count << 8 (ABORT: the workgroups with tickets below count run the
-// fallback).  Both are zeroed by the state setup that precedes the kernel on
+// kernel's fallback).  Both are zeroed by the state setup that precedes the kernel on
 // the stream.  `forced` > 0 makes the first arrival record ABORT with that
 // count at once (tests of the fallback).
 // A workgroup waits this long for the others before it records ABORT: a
@@ -53,24 +54,6 @@ __device__ inline int arrive_decide(int* coop, int n_groups, int forced, int tic
     else
       __builtin_amdgcn_s_sleep(2);
   }
-}
-
-// The whole layer for direction d by one workgroup alone: its waves walk the
-// units of each step with the per-step engine's wave body on the per-step
-// engine's state (h slots, cell state, GRU z and r*h, all set up by the state
-// setup), with a workgroup barrier between steps and between the two phases
-// of a GRU step with linear_before_reset = 0.
-template <typename T>
-__device__ __forceinline__ void fallback_direction(const StepArgs& a, int d) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int waves = int(blockDim.x) >> 6;
-  const int tasks = a.H * ((a.B + kRows - 1) / kRows);
-  const int phases = (a.cell == RNN_CELL_GRU && !a.lbr) ? 2 : 1;
-  for (int s = 0; s < a.steps; ++s)
-    for (int ph = 0; ph < phases; ++ph) {
-      for (int t = wave; t < tasks; t += waves) step_wave<T>(a, s, ph, t % a.H, (t / a.H) * kRows, d, lane);
-      __syncthreads();
-    }
 }
 
 }  // namespace rnnhip

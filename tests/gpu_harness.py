@@ -2,6 +2,7 @@
 every tensor, and compare against the CPU oracle."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -46,6 +47,12 @@ def gpu_layer(spec, inputs, engine="auto", offsets=None, outputs=None, layer=Non
         layer = rl.Layer(spec, engine=engine, device="cuda:0")
     layer.encode({**tens, **{n: o[0] for n, o in outs.items()}}, offsets=offs)
     torch.cuda.synchronize()
+    # a persistent step kernel must never end on its safety bound, and takes
+    # its fallback only when a test forces it
+    run = layer.run_status()
+    assert not run.timed_out, "a wait of the persistent step kernel passed its safety bound"
+    if not os.environ.get("RNN_PERSISTENT_FALLBACK"):
+        assert run.fallback_workgroups == 0, f"the fallback ran ({run.fallback_workgroups} workgroups)"
     res = {}
     for n, (buf, off, numel, shape) in outs.items():
         host = buf.cpu()

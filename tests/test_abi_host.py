@@ -107,10 +107,10 @@ def test_scratch_sizes(lib, cell, direction, G):
 def test_persistent_scratch_layout(lib, cell, lbr, direction):
     """The small-batch persistent engine's state scratch: two slots of tagged
     exchange words (and of r*h words for a GRU with linear_before_reset = 0),
-    the status word with the two residency words, and the per-step engine's
-    state (h slots, cell state, GRU buffers) for the fallback; each region
-    256-byte aligned.  One launch for the projection (with the setup), one for
-    every step."""
+    the status word with the two residency words, and what the fallback keeps
+    in memory where the fast path keeps registers (the cell state, a GRU's z
+    between its two phases); each region 256-byte aligned.  One launch for the
+    projection (with the setup), one for every step."""
     s = spec(cell, direction=direction, seq=7, batch=3, hidden=40, linear_before_reset=lbr)
     h = rl.rnn_problem_create(rl.make_desc(s, "persistent"))
     info = rl.rnn_problem_plan(h)
@@ -120,8 +120,8 @@ def test_persistent_scratch_layout(lib, cell, lbr, direction):
     dbh = D * 3 * 40
     al = lambda n: (n + 255) // 256 * 256
     gru = cell == "GRU"
-    want = (al(2 * dbh * 8) + (al(2 * dbh * 8) if gru and not lbr else 0) + al(3 * 4) + al(2 * dbh * 4)
-            + al(dbh * 4) + (2 * al(dbh * 4) if gru else 0))
+    want = (al(2 * dbh * 8) + (al(2 * dbh * 8) if gru and not lbr else 0) + al(3 * 4)
+            + al(dbh * 4) + (al(dbh * 4) if gru else 0))
     assert rl.rnn_scratch_size(h)[1] == want
     rl.rnn_problem_destroy(h)
 

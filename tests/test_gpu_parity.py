@@ -269,22 +269,24 @@ def _residency_words(layer, spec):
 
 
 # The persistent engine is launched plainly and its workgroups agree first
-# whether all of them run at once (GO), else the ones that arrived run the
-# layer one direction per workgroup (the fallback).  The fallback is forced
-# here with RNN_PERSISTENT_FALLBACK = k (k workgroups take part): every cell
-# and GRU form, lengths with 0, initial states, peepholes, clip,
-# input_forget, both dtypes (the vector-ALU and the matrix-core instances),
-# both layouts; then the residency words show which path ran.
-FALLBACK = [("LSTM", 0, "f32", 0), ("LSTM", 1, "f16", 1), ("GRU", 0, "f32", 1), ("GRU", 1, "f16", 0),
-            ("RNN", 0, "f32", 0), ("LSTM", 0, "f16", 0)]
+# whether all of them run at once (GO), else the ones that arrived take the
+# place of the whole grid in turn (the fallback), through the same products
+# and gate code.  The fallback is forced here with RNN_PERSISTENT_FALLBACK = k
+# (k workgroups take part): every cell and GRU form, lengths with 0, initial
+# states, peepholes, clip, input_forget, both dtypes (the vector-ALU and the
+# matrix-core instances), both layouts, one batch row (staggered polling).
+# Its outputs must be bit-identical to the fast path's; the residency words
+# and the library's run status show which path ran.
+FALLBACK = [("LSTM", 0, "f32", 0, 5), ("LSTM", 1, "f16", 1, 6), ("GRU", 0, "f32", 1, 5), ("GRU", 1, "f16", 0, 6),
+            ("RNN", 0, "f32", 0, 5), ("LSTM", 0, "f16", 0, 6), ("GRU", 0, "f16", 0, 4), ("LSTM", 0, "f32", 1, 1),
+            ("GRU", 0, "f32", 0, 1)]
 
 
-@pytest.mark.parametrize("cell,opt,dtype,layout", FALLBACK, ids=[f"{c}-{o}-{d}-L{l}" for c, o, d, l in FALLBACK])
+@pytest.mark.parametrize("cell,opt,dtype,layout,B", FALLBACK,
+                         ids=[f"{c}-{o}-{d}-L{l}-B{b}" for c, o, d, l, b in FALLBACK])
 @pytest.mark.parametrize("forced", ["1", "2"])
-def test_persistent_fallback(cell, opt, dtype, layout, forced, monkeypatch):
+def test_persistent_fallback(cell, opt, dtype, layout, B, forced, monkeypatch):
     import onnx_recurrent_layers_amd as rl
-    monkeypatch.setenv("RNN_PERSISTENT_FALLBACK", forced)
-    B = 5 if dtype == "f32" else 6
     spec = LayerSpec(cell, seq=10, batch=B, input=37, hidden=70, direction="bidirectional", layout=layout,
                      dtype=dtype, linear_before_reset=opt if cell == "GRU" else 0,
                      input_forget=opt if cell == "LSTM" else 0, peephole=cell == "LSTM", clip=2.5,
@@ -292,17 +294,19 @@ def test_persistent_fallback(cell, opt, dtype, layout, forced, monkeypatch):
     inp = make_inputs(spec, 61, Dists(sequence_lens=("I", 0, 10)))
     layer = rl.Layer(spec, engine="persistent", device="cuda:0")
     assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_blocks > 2
-    note(f"case persistent fallback {forced} {cell}/opt{opt}/{dtype}/L{layout}")
-    got = gpu_layer(spec, inp, layer=layer)
-    compare(spec, got, oracle.run(spec, inp, outputs=spec.outputs), what=f"fallback {forced} {cell}")
-    status, arrivals, decision = _residency_words(layer, spec)
-    assert status == 0 and decision == (2 | (int(forced) << 8)), (status, arrivals, decision)
-    # and without the switch, the fast path
-    monkeypatch.delenv("RNN_PERSISTENT_FALLBACK")
-    again = gpu_layer(spec, inp, layer=layer)
-    compare(spec, again, oracle.run(spec, inp, outputs=spec.outputs), what=f"persistent {cell}")
+    note(f"case persistent fallback {forced} {cell}/opt{opt}/{dtype}/L{layout}/B{B}")
+    fast = gpu_layer(spec, inp, layer=layer)
     status, arrivals, decision = _residency_words(layer, spec)
     assert status == 0 and decision == 1 and arrivals == layer.plan.step_blocks, (status, arrivals, decision)
+    compare(spec, fast, oracle.run(spec, inp, outputs=spec.outputs), what=f"persistent {cell}")
+    monkeypatch.setenv("RNN_PERSISTENT_FALLBACK", forced)
+    slow = gpu_layer(spec, inp, layer=layer)
+    status, arrivals, decision = _residency_words(layer, spec)
+    assert status == 0 and decision == (2 | (int(forced) << 8)), (status, arrivals, decision)
+    run = layer.run_status()
+    assert run.persistent == 1 and run.fallback_workgroups == int(forced) and run.timed_out == 0
+    for n in fast:
+        assert np.array_equal(fast[n].view(np.uint8), slow[n].view(np.uint8)), f"fallback {forced} {cell} {n}: bits differ"
 
 
 # One batch row on the persistent engine: the staggered polling (hidden sizes
@@ -476,15 +480,22 @@ def test_persistent_matrix_step_resident_r(cell, opt, B, H, layout, bidir, monke
 
 
 # The persistent matrix-core step's fallback (its grid not all running at
-# once, forced with RNN_PERSISTENT_FALLBACK = k): one workgroup per direction
-# runs the layer on the per-step engine's state.
-MFALL = [("LSTM", 1, "f16", 0), ("GRU", 0, "f16", 1), ("RNN", 0, "f32", 0)]
+# once, forced with RNN_PERSISTENT_FALLBACK = k): the workgroups that arrived
+# take the groups of tiles (one batch tile of one direction each) and run
+# every tile of a group in turn through the same tile body.  Every mode: f16
+# with split h (resident R and streamed R, both GRU forms), f32, and f32 on
+# the bf16 matrix cores.  Bit-identical to the fast path.
+MFALL = [("LSTM", 1, "f16", 0, None), ("GRU", 0, "f16", 1, None), ("GRU", 1, "f16", 0, None),
+         ("RNN", 0, "f32", 0, None), ("LSTM", 0, "f32", 1, "1"), ("LSTM", 0, "f16", 1, None)]
 
 
-@pytest.mark.parametrize("cell,opt,dtype,layout", MFALL, ids=[f"{c}-{o}-{d}-L{l}" for c, o, d, l in MFALL])
+@pytest.mark.parametrize("cell,opt,dtype,layout,split", MFALL,
+                         ids=[f"{c}-{o}-{d}-L{l}-split{s}" for c, o, d, l, s in MFALL])
 @pytest.mark.parametrize("forced", ["1", "2"])
-def test_persistent_matrix_step_fallback(cell, opt, dtype, layout, forced, monkeypatch):
+def test_persistent_matrix_step_fallback(cell, opt, dtype, layout, split, forced, monkeypatch):
     import onnx_recurrent_layers_amd as rl
+    if split is not None:
+        monkeypatch.setenv("RNN_F32_SPLIT", split)
     spec = LayerSpec(cell, seq=6, batch=20, input=24, hidden=40, direction="bidirectional", layout=layout,
                      dtype=dtype, linear_before_reset=opt if cell == "GRU" else 0,
                      input_forget=opt if cell == "LSTM" else 0, init_h=True, init_c=cell == "LSTM", lens=True,
@@ -492,8 +503,16 @@ def test_persistent_matrix_step_fallback(cell, opt, dtype, layout, forced, monke
     layer = rl.Layer(spec, engine="persistent", device="cuda:0")
     assert layer.plan.engine == rl.ENGINES["persistent"] and layer.plan.step_launches == 1
     inp = make_inputs(spec, 83, Dists(sequence_lens=("I", 0, 6), W=("U", -0.2, 0.2), R=("U", -0.1, 0.1)))
+    note(f"case matrix-core fallback {forced} {cell}/opt{opt}/{dtype}/L{layout}/split{split}")
+    fast = check(spec, inp, engine="persistent", what=f"matrix-core fast {cell}")
+    fast = gpu_layer(spec, inp, layer=layer)
+    assert layer.run_status().fallback_workgroups == 0
     monkeypatch.setenv("RNN_PERSISTENT_FALLBACK", forced)
-    check(spec, inp, engine="persistent", what=f"matrix-core fallback {forced} {cell}")
+    slow = gpu_layer(spec, inp, layer=layer)
+    run = layer.run_status()
+    assert run.persistent == 1 and run.fallback_workgroups == int(forced) and run.timed_out == 0
+    for n in fast:
+        assert np.array_equal(fast[n].view(np.uint8), slow[n].view(np.uint8)), f"fallback {forced} {cell} {n}: bits differ"
 
 
 def test_large_batch_general_activations():
@@ -569,6 +588,76 @@ def test_lengths_edge_cases_and_max_length(engine):
         check(spec.replace(max_length=4), inp, engine=engine, what=f"max_length {cell}")
 
 
+# MaxLength ("Recurrent layers" page: a host-side bound on the sequence
+# lengths that shortens the step loop) below some rows' lengths, and below
+# Seq with no lengths at all, on every step engine: the vector-ALU persistent
+# engine, one launch per step, the matrix-core step (18 rows, f32) and its
+# persistent form (16 rows, f16, default activations).
+MAXLEN_CASES = [("launch", 5, "f32", None), ("persistent", 5, "f32", None), ("auto", 18, "f32", None),
+                ("persistent", 16, "f16", "default")]
+
+
+@pytest.mark.parametrize("engine,B,dtype,acts", MAXLEN_CASES, ids=[f"{e}-B{b}-{d}" for e, b, d, _ in MAXLEN_CASES])
+def test_max_length_cuts_rows(engine, B, dtype, acts):
+    for cell in ("LSTM", "GRU", "RNN"):
+        for lbr in ((0, 1) if cell == "GRU" else (0,)):
+            spec = LayerSpec(cell, seq=6, batch=B, input=12, hidden=48, direction="bidirectional", dtype=dtype,
+                             init_h=True, init_c=cell == "LSTM", lens=True, linear_before_reset=lbr, max_length=4)
+            inp = make_inputs(spec, 13)
+            lens = np.array([6, 0, 5, 17, -2, 4, 3, 1] * 3, np.int32)[:B]   # rows above, at and below 4
+            inp["sequence_lens"] = lens
+            check(spec, inp, engine=engine, what=f"max_length 4 rows cut {cell} lbr{lbr}")
+            nolens = spec.replace(lens=False)
+            inp.pop("sequence_lens")
+            check(nolens, inp, engine=engine, what=f"max_length 4 < Seq 6 without lengths {cell} lbr{lbr}")
+
+
+# f16 outputs are rounded to nearest even once ("How a layer runs", item 4).
+# With W = R = 0 and Affine activations, a unit's output is exactly the f32
+# sum Wb + Rb (forward, alpha 1) or half of it (reverse, alpha 0.5); the bias
+# pairs put that value on ties between binary16 neighbours (both parities),
+# just off them, past the largest finite value, in the subnormal range and at
+# its edge.  Every output must carry exactly the bits of the oracle's
+# round-to-nearest-even of the same value.
+_HALF_PAIRS = [(1.0, 2.0 ** -11), (1.0 + 2.0 ** -10, 2.0 ** -11), (1.0, 2.0 ** -12), (1.0, 3 * 2.0 ** -12),
+               (65504.0, 16.0), (65504.0, 16.0 - 2.0 ** -7), (-1.0, -(2.0 ** -11)), (3 * 2.0 ** -24, 0.0),
+               (2.0 ** -24, 0.0), (2.0 ** -14, -(2.0 ** -24)), (2048.0, 1.0), (2048.0, 3.0), (-65504.0, -32.0),
+               (0.0, -0.0), (-(2.0 ** -24), 0.0)]
+
+
+def _half_bias_pairs(n_random, seed):
+    rng = np.random.default_rng(seed)
+    pairs = list(_HALF_PAIRS)
+    # random pairs within eleven binades, so that their sum is exact in f32
+    mag = rng.uniform(-8, 2, size=(n_random, 2))
+    v = (np.sign(rng.uniform(-1, 1, size=(n_random, 2))) * 2.0 ** mag).astype(np.float16).astype(np.float64)
+    pairs += [tuple(r) for r in v]
+    return np.array(pairs, np.float64)
+
+
+@pytest.mark.parametrize("engine,B,layout", [("persistent", 1, 0), ("launch", 3, 1), ("auto", 16, 0)])
+def test_f16_outputs_round_to_nearest_even(engine, B, layout):
+    pairs = _half_bias_pairs(49, 5)
+    H = len(pairs)
+    spec = LayerSpec("RNN", seq=3, batch=B, input=7, hidden=H, direction="bidirectional", layout=layout,
+                     dtype="f16", acts=(("Affine", 1.0, 0.0), ("Affine", 0.5, 0.0)), outputs=("Y", "Y_h"))
+    inp = make_inputs(spec, 3)
+    inp["W"] = np.zeros_like(inp["W"])
+    inp["R"] = np.zeros_like(inp["R"])
+    bias = np.concatenate([pairs[:, 0], pairs[:, 1]]).astype(np.float16)
+    assert np.array_equal(bias.astype(np.float64), np.concatenate([pairs[:, 0], pairs[:, 1]])), "pairs not in f16"
+    inp["B"] = np.stack([bias, bias])
+    note(f"case f16 rounding engine={engine} B={B} L{layout} H={H}")
+    got = gpu_layer(spec, inp, engine=engine)
+    ref = oracle.run(spec, inp, outputs=spec.outputs)
+    for n in ("Y", "Y_h"):
+        want = oracle.round_half(ref[n])
+        have = got[n].view(np.uint16)
+        bad = np.argwhere(have != want)
+        assert bad.size == 0, (f"{n}{tuple(bad[0])}: value {ref[n][tuple(bad[0])]!r} gave bits "
+                               f"{have[tuple(bad[0])]:#06x}, nearest-even is {want[tuple(bad[0])]:#06x}")
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 def test_batch_above_eight_and_hidden_not_dividing(engine):
     for cell, H in (("LSTM", 65), ("GRU", 127), ("RNN", 129)):
@@ -582,7 +671,9 @@ def test_batch_above_eight_and_hidden_not_dividing(engine):
 # ---------------------------------------------------------------------------
 FULL = [("C1", {}), ("C2", {}), ("C3", {"linear_before_reset": 0}), ("C3", {"linear_before_reset": 1}),
         ("C4", {}), ("C5", {}), ("C4", {"engine": "launch"}), ("C5", {"engine": "persistent"})]
-SAMPLE_ROWS = {"C4": [0, 9, 31, 63], "C5": [0, 255]}
+# one row in each batch tile of the step kernels (C4: 16-row tiles; C5:
+# 64-row tiles), every unit of each sampled row
+SAMPLE_ROWS = {"C4": [0, 21, 42, 63], "C5": [0, 100, 170, 255]}
 
 
 # The recognizer shapes of the "Recurrent layers" page: both layer shapes,
