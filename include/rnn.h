@@ -189,6 +189,23 @@ int rnn_encode(const rnn_problem* problem, const rnn_operands* operands,
 int rnn_encode_timed(const rnn_problem* problem, const rnn_operands* operands,
                      void* xw_scratch, void* state_scratch, void* stream, void* const events[5]);
 
+/* rnn_encode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * projection and state scratch come from a fixed device array of
+ * RNN_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * (allocated when the library's code is loaded on that device, released when
+ * the process ends); the caller still passes inputs and outputs.  The layer
+ * runs on the device current on the calling thread, which must be the
+ * stream's device.  Nothing is allocated and nothing needs clearing: each call
+ * writes every scratch value its results depend on.  All calls on one device share that
+ * device's array, so calls that overlap in time on one device race: order
+ * them on one stream (or with an event).  Errors as rnn_encode, plus
+ * RNN_ERR_UNSUPPORTED when the layer's scratch (rnn_scratch_size: the two
+ * sizes, each rounded up to 256 bytes) exceeds RNN_NOALLOC_SCRATCH_BYTES; as
+ * with rnn_encode, nothing is enqueued when a check fails. */
+#define RNN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int rnn_encode_noalloc(const rnn_problem* problem, const rnn_operands* operands, void* stream);
+
 /* Host-side check of sequence lengths (the page asks callers to validate them
  * on the host): every value in [0, seq].  On success *max_len_out (if not
  * NULL) receives the largest length, usable as max_length. */

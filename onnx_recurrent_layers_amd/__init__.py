@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH):
     lib.rnn_validate_lengths.restype = ctypes.c_int
     lib.rnn_problem_plan.argtypes = [ctypes.c_void_p, P(rnn_plan_info)]
     lib.rnn_problem_plan.restype = ctypes.c_int
+    lib.rnn_encode_noalloc.argtypes = [ctypes.c_void_p, P(rnn_operands), ctypes.c_void_p]
+    lib.rnn_encode_noalloc.restype = ctypes.c_int
     lib.rnn_read_run_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P(rnn_run_status)]
     lib.rnn_read_run_status.restype = ctypes.c_int
     lib.rnn_last_error.argtypes = []
@@ -208,6 +210,14 @@ def rnn_encode(handle, operands: rnn_operands, xw_scratch_ptr: int, state_scratc
                stream_ptr: int = 0) -> None:
     _check(load_library().rnn_encode(handle, ctypes.byref(operands), ctypes.c_void_p(xw_scratch_ptr or None),
                                      ctypes.c_void_p(state_scratch_ptr or None), ctypes.c_void_p(stream_ptr or None)))
+
+
+def rnn_encode_noalloc(handle, operands: rnn_operands, stream_ptr: int = 0) -> None:
+    """rnn_encode with the library's fixed scratch (no caller scratch)."""
+    _check(load_library().rnn_encode_noalloc(handle, ctypes.byref(operands), ctypes.c_void_p(stream_ptr or None)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 def rnn_encode_timed(handle, operands: rnn_operands, xw_scratch_ptr: int, state_scratch_ptr: int,

@@ -362,6 +362,17 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
 
 }  // namespace
 
+namespace rnnhip {
+
+int encode_layer(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
+                 void* stream) {
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr);
+}
+
+int set_error(int code, int cell, const char* msg) { return fail(code, cell, "%s", msg); }
+
+}  // namespace rnnhip
+
 extern "C" int rnn_encode(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch,
                           void* state_scratch, void* stream) {
   return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr);

@@ -151,6 +151,12 @@ struct PersistentIO {
   int* status;
 };
 
+// rnn_encode with the scratch pointers already chosen (api.cpp), and the
+// thread's error message set from another file.
+int encode_layer(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
+                 void* stream);
+int set_error(int code, int cell, const char* msg);
+
 hipError_t launch_projection(const ProjArgs& a, const SetupArgs& sa, int dtype, hipStream_t s);  // also runs the state setup
 hipError_t launch_setup(const SetupArgs& a, hipStream_t s);
 hipError_t launch_split_r(const void* R, unsigned short* rsplit, int64_t n, hipStream_t s);
