@@ -211,13 +211,25 @@ int rnn_encode_noalloc(const rnn_problem* problem, const rnn_operands* operands,
  * NULL) receives the largest length, usable as max_length. */
 int rnn_validate_lengths(const int32_t* host_lens, int64_t batch, int64_t seq, int64_t* max_len_out);
 
-/* What rnn_encode will launch for this problem. */
+/* What rnn_encode will launch for this problem, and which arithmetic units
+ * carry its products (for measurement against the right peak). */
+typedef enum {
+  RNN_PRODUCTS_F32_VALU = 0,   /* f32 fused multiply-adds on the vector ALUs */
+  RNN_PRODUCTS_F32_MFMA = 1,   /* f32 matrix cores */
+  RNN_PRODUCTS_F16_MFMA = 2,   /* f16 matrix cores, f32 accumulation; in the steps h as two f16 halves
+                                  (two products per product of the method) */
+  RNN_PRODUCTS_BF16X3_MFMA = 3 /* bf16 matrix cores, each f32 product as three bf16 products */
+} rnn_products;
 typedef struct {
   int32_t engine;          /* rnn_engine actually used */
   int32_t steps;           /* number of recurrent steps run (max_length or S) */
-  int32_t launches;        /* kernel launches per rnn_encode */
+  int32_t launches;        /* kernel launches per rnn_encode (with the persistent engine, one of them is
+                              the fallback kernel that follows the step kernel and exits at once
+                              unless the step kernel's grid was not all resident) */
   int32_t step_blocks;     /* workgroups of the persistent step kernel (0 for the per-step engine) */
-  int32_t step_launches;   /* launches of the recurrent-step stage per rnn_encode */
+  int32_t step_launches;   /* launches of the recurrent-step kernel per rnn_encode */
+  int32_t proj_products;   /* rnn_products of the input projection */
+  int32_t step_products;   /* rnn_products of the recurrent products (R * h) */
 } rnn_plan_info;
 int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info);
 

@@ -66,7 +66,12 @@ class rnn_run_status(ctypes.Structure):
 
 class rnn_plan_info(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("steps", ctypes.c_int32), ("launches", ctypes.c_int32),
-                ("step_blocks", ctypes.c_int32), ("step_launches", ctypes.c_int32)]
+                ("step_blocks", ctypes.c_int32), ("step_launches", ctypes.c_int32),
+                ("proj_products", ctypes.c_int32), ("step_products", ctypes.c_int32)]
+
+
+# rnn_products: which arithmetic units carry a stage's products
+PRODUCTS = {0: "f32 vector ALU", 1: "f32 matrix cores", 2: "f16 matrix cores", 3: "bf16x3 matrix cores"}
 
 
 _lib = None

@@ -304,10 +304,26 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
     n += 1;                        // projection with the state setup (or the setup alone when Seq = 0); the
                                    // steps and the setup write the outputs
     if (p->S > 0) n += step_launch_count(*p);
+    if (p->S > 0 && p->steps > 0 && p->engine == RNN_ENGINE_PERSISTENT) n += 1;   // the fallback kernel
     if (p->S > 0 && p->f32_split_step) n += 1;   // R split into bf16 planes
   }
   info->launches = n;
   info->step_launches = (p->B > 0 && p->S > 0) ? step_launch_count(*p) : 0;
+  // projection: f16 tensors on the f16 matrix cores; f32 tensors on the f32
+  // matrix cores or as three bf16 products
+  info->proj_products = p->desc.dtype == RNN_DTYPE_F16 ? RNN_PRODUCTS_F16_MFMA
+                        : p->f32_split_proj ? RNN_PRODUCTS_BF16X3_MFMA : RNN_PRODUCTS_F32_MFMA;
+  // steps: the small-batch persistent engine uses the f16 matrix cores for f16
+  // layers with the default activations and 3 to 8 rows (padded to 4 or 8),
+  // else vector-ALU products; the matrix-core step (16 rows and more) runs in
+  // its mode; the per-step engine for other batches uses the vector ALUs
+  if (p->engine == RNN_ENGINE_PERSISTENT && !p->pers_mfma)
+    info->step_products = (p->esize == 2 && p->def_acts && p->B >= 3) ? RNN_PRODUCTS_F16_MFMA : RNN_PRODUCTS_F32_VALU;
+  else if (mfma_step_supported(*p))
+    info->step_products = p->f32_split_step ? RNN_PRODUCTS_BF16X3_MFMA
+                          : (p->esize == 2 && p->def_acts) ? RNN_PRODUCTS_F16_MFMA : RNN_PRODUCTS_F32_MFMA;
+  else
+    info->step_products = RNN_PRODUCTS_F32_VALU;
   return RNN_OK;
 }
 

@@ -816,44 +816,23 @@ struct PersDmaArgs {
   int* flags;           // one per workgroup: phases finished; zeroed by the state setup
   int* status;          // [0] set to 1 if a wait ran past its bound; [1], [2] residency (residency.h)
   int fallback;         // > 0: take the fallback with this many workgroups (tests)
+  int gx, gy, gz;       // the tile grid: unit tiles, batch tiles, directions
 };
 
 constexpr long kFlagSpinLimit = 1l << 22;
 
 template <int MODE, int BM, int CB, bool RR>
 __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p) {
-  // launched plainly: every workgroup running (GO), or the workgroups that
-  // arrived run every tile in turn (below; residency.h)
-  __shared__ int coop_dec, coop_ticket;
+  // launched plainly: every workgroup running (GO), or every workgroup exits
+  // and the fallback kernel that follows runs the layer (residency.h)
+  __shared__ int coop_dec;
   if (threadIdx.x == 0) {
     const int t = arrive_ticket(p.status + 1);
     coop_dec = arrive_decide(p.status + 1, int(gridDim.x * gridDim.y * gridDim.z), p.fallback, t);
-    coop_ticket = t;
   }
   __syncthreads();
+  if (__builtin_expect(coop_dec != 1, 0)) return;
   const int steps = p.ph[0].a.steps, P = p.P;
-  if (__builtin_expect(coop_dec != 1, 0)) {
-    // Fallback: the tiles of one batch tile and direction depend only on one
-    // another, so the workgroups that arrived take such groups (group g =
-    // batch tile + tiles_y * direction, the ticket's groups g = ticket,
-    // ticket + count, ...) and run every tile of a group in turn, step by
-    // step and phase by phase, through the same tile body as the fast path:
-    // the results are bit-identical.  One workgroup's own stores are complete
-    // (and so visible to its later loads) after each tile's final wait.
-    const int cnt = coop_dec >> 8;
-    const int gx = int(gridDim.x), gy = int(gridDim.y);
-    const int groups = gy * int(gridDim.z);
-    for (int g = coop_ticket; coop_ticket < cnt && g < groups; g += cnt)
-      for (int s = 0; s < steps; ++s)
-        for (int ph = 0; ph < P; ++ph)
-          for (int x = 0; x < gx; ++x) {
-            if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s, x, g % gy, g / gy, true);
-            else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s, x, g % gy, g / gy, true);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-            __syncthreads();
-          }
-    return;
-  }
   __shared__ int abort_s;
   const int gx = int(gridDim.x);
   const int row = int(blockIdx.y + gridDim.y * blockIdx.z);   // batch tile and direction
@@ -890,6 +869,35 @@ __global__ __launch_bounds__(kMThreads) void step_dma_pers_kernel(PersDmaArgs p)
     }
 }
 
+// Enqueued right after step_dma_pers_kernel, one workgroup per group of
+// tiles (one batch tile of one direction): on GO it exits at once; on ABORT
+// with count k, workgroups 0..k-1 take the groups g = w, w+k, ... and run
+// every tile of a group in turn, step by step and phase by phase, through the
+// same tile body as the fast path, so the results are bit-identical.  The
+// tiles of one group depend only on one another, and one workgroup's own
+// stores are complete (and so visible to its later loads) after each tile's
+// final wait.  It waits on no other workgroup.
+template <int MODE, int BM, int CB, bool RR>
+__global__ __launch_bounds__(kMThreads) void step_dma_fallback_kernel(PersDmaArgs p) {
+  __shared__ int dec;
+  if (threadIdx.x == 0) dec = __hip_atomic_load(p.status + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (dec < 2) return;
+  const int cnt = dec >> 8;
+  const int steps = p.ph[0].a.steps, P = p.P;
+  const int groups = p.gy * p.gz;
+  if (int(blockIdx.x) >= cnt) return;
+  for (int g = int(blockIdx.x); g < groups; g += cnt)
+    for (int s = 0; s < steps; ++s)
+      for (int ph = 0; ph < P; ++ph)
+        for (int x = 0; x < p.gx; ++x) {
+          if (ph == 0) dma_step<MODE, BM, CB, true, RR>(p.ph[0], s, x, g % p.gy, g / p.gy, true);
+          else dma_step<MODE, BM, CB, true, RR>(p.ph[1], s, x, g % p.gy, g / p.gy, true);
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+          __syncthreads();
+        }
+}
+
 template <int MODE, int BM, int CB>
 static hipError_t launch_cfg(const MfmaStepArgs& m, hipStream_t s) {
   const StepArgs& a = m.a;
@@ -918,13 +926,16 @@ static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
   const dim3 grid(unsigned((a.H + pa.ph[0].UJ - 1) / pa.ph[0].UJ), unsigned((a.B + BM - 1) / BM), unsigned(a.D));
   auto kern = step_dma_pers_kernel<MODE, BM, CB, RR>;
   PersDmaArgs arg = pa;
+  arg.gx = int(grid.x);
+  arg.gy = int(grid.y);
+  arg.gz = int(grid.z);
   // A plain launch after a host check that every workgroup fits on the device
   // at once; the kernel settles residency itself (residency.h).
   // RNN_COOPERATIVE_LAUNCH=1 takes the cooperative launch instead.
   const char* coop_env = std::getenv("RNN_COOPERATIVE_LAUNCH");
+  hipError_t e;
   if (!(coop_env && coop_env[0] == '1')) {
     int per_cu = 0, dev = 0, cus = 0;
-    hipError_t e;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kMThreads,
                                                            0)) != hipSuccess)
       return e;
@@ -932,10 +943,15 @@ static hipError_t launch_pers_cfg(const PersDmaArgs& pa, hipStream_t s) {
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     if (int64_t(per_cu) * cus < int64_t(grid.x) * grid.y * grid.z) return hipErrorCooperativeLaunchTooLarge;
     hipLaunchKernelGGL(kern, grid, dim3(kMThreads), 0, s, arg);
-    return hipGetLastError();
+    e = hipGetLastError();
+  } else {
+    void* args[] = {&arg};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), grid, dim3(kMThreads), args, 0u, s);
   }
-  void* args[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), grid, dim3(kMThreads), args, 0u, s);
+  if (e != hipSuccess) return e;
+  // the fallback (it exits at once unless the decision was ABORT)
+  hipLaunchKernelGGL((step_dma_fallback_kernel<MODE, BM, CB, RR>), dim3(grid.y * grid.z), dim3(kMThreads), 0, s, arg);
+  return hipGetLastError();
 }
 
 // Resident R (f16 mode, one phase per step, 16 or 32 batch rows): the

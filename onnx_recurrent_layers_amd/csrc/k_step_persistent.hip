@@ -17,10 +17,13 @@
 // each takes an arrival ticket; the first to see every ticket taken records
 // GO, and one that waits past a short window records ABORT with the number of
 // tickets taken by then (one compare-and-swap decides).  On GO the fast path
-// below runs.  On ABORT (the device was partly held by other work) the
-// workgroups that had arrived run the layer one direction per workgroup,
-// which needs no other workgroup: slower, but correct, and never a wait on a
-// workgroup that may not be scheduled.
+// below runs.  On ABORT (the device was partly held by other work) every
+// workgroup exits, and the fallback kernel that the host enqueues right after
+// this one (it exits at once on GO) runs the layer one direction per
+// workgroup, taking the place of each workgroup of the direction in turn with
+// the same arithmetic: slower, but bit-identical, and never a wait on a
+// workgroup that may not be scheduled.  The fallback lives in its own kernel
+// because inlined here it cost the fast path 2-3 % (C3: 877 against 859 us).
 //
 // Exchange: the hidden state of step s travels as 64-bit words
 // (tag = step << 32 | f32 bits) stored and loaded with agent-scope relaxed
@@ -463,8 +466,10 @@ __device__ __forceinline__ void load_rows(const PersArgs& p, T* Rl, int RS, int 
 }
 
 // Gate arithmetic of one (unit, batch row) element in the step's first (or
-// only) phase, in the order of cells.h.  Shared by the fast path and the
-// fallback, so that both take exactly the same operations.  rec_of(gi) is
+// only) phase, in the order of cells.h: the fallback's copy of the fast path's
+// inline gate code, the same expressions over the same helpers (the fast path
+// keeps its inline form, which measured 1.5-2 % faster per step); a GPU test
+// requires the two paths' outputs bit for bit equal.  rec_of(gi) is
 // the recurrent sum of computed gate block gi; xv, wb, rb hold the
 // projection and biases of gate block g at index g.  Returns the new h
 // (LSTM, RNN, GRU with linear_before_reset = 1; c is updated in place); for
@@ -694,7 +699,12 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   };
 
   // R rows of this workgroup's units, resident for the whole layer
-  load_rows<T>(p, Rl, RS, d, u0, Uw, H4);
+  const T* Rd = static_cast<const T*>(a.R) + int64_t(d) * GH * H;
+  for (int e = tid; e < p.NR * H4; e += kPThreads) {
+    const int r = e / H4, k = e - r * H4;
+    const int gi = r / p.U, uu = r - gi * p.U;
+    Rl[r * RS + k] = (uu < Uw && k < H) ? Rd[int64_t(p.gate_of[gi] * H + u0 + uu) * H + k] : T(0.f);
+  }
   // padded tail of h stays zero (the f16 planes are cleared whole: columns of
   // absent batch rows feed only dropped outputs, but must not hold Inf or NaN)
   if constexpr (MF) {
@@ -703,24 +713,11 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     for (int e = NB * H + tid; e < NB * H4; e += kPThreads) static_cast<float*>(hs)[e] = 0.f;
   }
 
-  // every workgroup running, or the fallback
-  __shared__ int coop_dec, coop_ticket;
-  if (tid == 0) {
-    coop_dec = arrive_decide(p.status + 1, int(gridDim.x), p.fallback, ticket);
-    coop_ticket = ticket;
-  }
+  // every workgroup running, or the fallback kernel that follows this one
+  __shared__ int coop_dec;
+  if (tid == 0) coop_dec = arrive_decide(p.status + 1, int(gridDim.x), p.fallback, ticket);
   __syncthreads();
-  // (marked unlikely so that the compiler lays the fallback's code out after
-  // the main path: placed before it, the fallback moved the step loop's code
-  // and cost C2 3 % per layer)
-  if (__builtin_expect(coop_dec != 1, 0)) {
-    const int cnt = coop_dec >> 8;
-    int fail = 0;
-    if (coop_ticket < cnt)
-      for (int dd = coop_ticket; dd < a.D && !fail; dd += cnt) fail = fallback_blocks<T, NB, DEF>(p, dd, smem);
-    if (fail && tid == 0) atomicExch(p.status, 1);
-    return;
-  }
+  if (__builtin_expect(coop_dec != 1, 0)) return;
 
   int maxL = 0;
   unsigned lens_left[NB];
@@ -848,10 +845,32 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
     // 3. gate arithmetic
     float hnew = 0.f, z = 0.f;
     if (live) {
-      float rh = 0.f;
-      hnew = gates_first<DEF>(a, p.cand, acts, xv, [&](int gi) { return recv(gi * p.U + g_uu, g_b); }, wb, rb, peep,
-                              c, hown, z, rh);
-      if (p.cand >= 0) put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), rh);
+      auto pre = [&](int gi, int g) { return pre_sum(xv[g], recv(gi * p.U + g_uu, g_b), wb[g], rb[g]); };
+      if (a.cell == RNN_CELL_LSTM) {
+        float p4[4];
+        p4[0] = pre(0, 0);
+        p4[1] = pre(1, 1);
+        if (a.input_forget) {
+          p4[2] = 0.f;
+          p4[3] = pre(2, 3);
+        } else {
+          p4[2] = pre(2, 2);
+          p4[3] = pre(3, 3);
+        }
+        lstm_unit<DEF>(p4, a.P ? peep : nullptr, c, a.clip, a.input_forget, acts, &hnew, &c);
+      } else if (a.cell == RNN_CELL_GRU) {
+        z = gru_gate<DEF>(pre(0, 0), a.clip, acts);
+        const float r = gru_gate<DEF>(pre(1, 1), a.clip, acts);
+        if (p.cand < 0) {
+          // linear_before_reset = 1: h~ = g(xw_h + r * (rec_h + Rb_h) + Wb_h)
+          const float ph = (xv[2] + r * (recv(2 * p.U + g_uu, g_b) + rb[2])) + wb[2];
+          hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
+        } else {
+          put_word(a.xch2 + (s & 1) * DBH + dBH + int64_t(g_b) * H + j, unsigned(s), r * hown);
+        }
+      } else {
+        hnew = rnn_unit<DEF>(pre(0, 0), a.clip, acts);
+      }
     }
 
     if (p.cand >= 0) {
@@ -863,7 +882,11 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
       if ((abort_run = abort_flag) != 0) break;
       run_products(p.cand * p.U, p.NR);
       lds_barrier();
-      if (live) hnew = gates_cand<DEF>(a, acts, xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2], z, hown);
+      if (live) {
+        // h~ = g(((xw_h + R_h.(r*h)) + Wb_h) + Rb_h)
+        const float ph = pre_sum(xv[2], recv(p.cand * p.U + g_uu, g_b), wb[2], rb[2]);
+        hnew = gru_unit<DEF>(z, ph, hown, a.clip, acts);
+      }
     }
 
     if (live) {
@@ -884,6 +907,24 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   }
   if (!abort_run && p.Y) store_y();
   if (abort_run && tid == 0) atomicExch(p.status, 1);
+}
+
+// Enqueued right after persistent_kernel, one workgroup per direction: on GO
+// (the decision word is final once that kernel has ended) it exits at once;
+// on ABORT with count k, workgroups 0..k-1 run the directions d = w, w+k, ...
+// (fallback_blocks).  It waits on no other workgroup.
+template <typename T, int NB, bool DEF>
+__global__ __launch_bounds__(kPThreads) void persistent_fallback_kernel(PersArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int dec;
+  if (threadIdx.x == 0) dec = __hip_atomic_load(p.status + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (dec < 2) return;
+  const int cnt = dec >> 8;
+  if (int(blockIdx.x) >= cnt) return;
+  int fail = 0;
+  for (int dd = blockIdx.x; dd < p.a.D && !fail; dd += cnt) fail = fallback_blocks<T, NB, DEF>(p, dd, smem);
+  if (fail && threadIdx.x == 0) atomicExch(p.status, 1);
 }
 
 namespace {
@@ -947,9 +988,13 @@ bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per
 template <typename T, int NB, bool DEF>
 static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStream_t s) {
   auto kern = persistent_kernel<T, NB, DEF>;
+  auto fk = persistent_fallback_kernel<T, NB, DEF>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(fk), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               int(lds))) != hipSuccess)
+    return e;
   PersArgs arg = pa;
   // A plain launch after checking on the host that every workgroup fits on
   // the device at once; the kernel itself settles whether they all run
@@ -965,11 +1010,16 @@ static hipError_t launch_nb(const PersArgs& pa, int blocks, size_t lds, hipStrea
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     if (per_cu * cus < blocks) return hipErrorCooperativeLaunchTooLarge;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(kPThreads), lds, s, arg);
-    return hipGetLastError();
+    e = hipGetLastError();
+  } else {
+    void* args[] = {&arg};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(blocks), dim3(kPThreads), args,
+                                   unsigned(lds), s);
   }
-  void* args[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(blocks), dim3(kPThreads), args,
-                                    unsigned(lds), s);
+  if (e != hipSuccess) return e;
+  // the fallback (it exits at once unless the decision was ABORT)
+  hipLaunchKernelGGL(fk, dim3(pa.a.D), dim3(kPThreads), lds, s, arg);
+  return hipGetLastError();
 }
 
 hipError_t launch_step_persistent(const StepArgs& a, const Problem& p, const PersistentIO& io, hipStream_t s) {

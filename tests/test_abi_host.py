@@ -114,7 +114,7 @@ def test_persistent_scratch_layout(lib, cell, lbr, direction):
     s = spec(cell, direction=direction, seq=7, batch=3, hidden=40, linear_before_reset=lbr)
     h = rl.rnn_problem_create(rl.make_desc(s, "persistent"))
     info = rl.rnn_problem_plan(h)
-    assert info.engine == rl.ENGINES["persistent"] and info.step_launches == 1 and info.launches == 2
+    assert info.engine == rl.ENGINES["persistent"] and info.step_launches == 1 and info.launches == 3
     assert info.step_blocks > 0
     D = 2 if direction == "bidirectional" else 1
     dbh = D * 3 * 40

@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 def test_bench_line(monkeypatch, capsys):
     note("case bench.main() C2 steps 3 warmup 1 cpu-seconds 0.5")
-    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5"])
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5",
+                                      "--extra", "C1,C3", "--extra-cpu-seconds", "0.3"])
     assert bench.main() == 0
     out = capsys.readouterr().out.strip().splitlines()
     d = json.loads(out[-1])
@@ -43,3 +44,26 @@ def test_bench_line(monkeypatch, capsys):
 
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "timesteps/s" and c["cores"] >= 1 and c["value"] > 0
+    assert c["host_cores"] >= 1 and c["cpu_model"]
+    assert d["cpu_baseline_single_thread"]["cores"] == 1
+
+    # every fraction against a peak or a floor is at most 1
+    for b in d["step_bounds"].values():
+        assert 0 < b["frac"] <= 1.0, b
+    assert d["roofline"]["binding"] in d["step_bounds"]
+    p = d["projection"]
+    assert p["units"] == "f32 matrix cores" and p["issued_flops"] == p["method_flops"]
+    assert 0 < p["frac"] <= 1.0
+    assert p["method_flops"] == 2.0 * 2 * spec.seq * spec.batch * 4 * spec.hidden * spec.input
+
+    # the other workloads, each with the same figures
+    assert set(d["configs"]) == {"C1", "C3"}
+    c3 = d["configs"]["C3"]
+    s3 = synth.CONFIGS["C3"]["spec"]
+    assert c3["timesteps_per_layer"] == s3.seq and c3["step_products"] == "f16 matrix cores"
+    assert c3["timesteps_per_s"] == pytest.approx(s3.seq / (c3["layer_ms"] / 1000.0), rel=1e-3)
+    for r in d["configs"].values():
+        for b in r["step_bounds"].values():
+            assert 0 < b["frac"] <= 1.0, b
+        assert 0 < r["projection"]["frac"] <= 1.0
+        assert r["cpu_baseline"]["value"] > 0 and r["fallback_workgroups"] == 0
