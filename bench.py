@@ -293,10 +293,14 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
     method = step_flops(spec) * n_steps / step_launches
     issued = method * (2 if step_kind == "f16 matrix cores" else ISSUED_PER_PRODUCT[step_kind])
     mf = issued / (launch_ms / 1000.0) / 1e12
+    prof = TRAFFIC_PROFILES.get((name, engine_name))
     bounds = {
         "hbm": {"achieved": round(hbm, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm / HBM_PEAK_GBS, 5),
                 "bytes_per_launch": int(bytes_per_launch),
-                "what": "algorithmic bytes: R once per step, the step's Xw slice, h (and c) read and written"},
+                "traffic": profiled_traffic(prof) if prof else None,
+                "what": "algorithmic bytes: R once per step, the step's Xw slice, h (and c) read and written; "
+                        "traffic: measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a "
+                        "plain copy) while the kernel sources match the profiled ones"},
         "arith": {"achieved": round(mf, 3), "peak": PEAK_TFLOPS[step_kind], "unit": "TFLOP/s",
                   "frac": round(mf / PEAK_TFLOPS[step_kind], 5), "units": step_kind,
                   "method_flops_per_launch": method, "issued_flops_per_launch": issued},
@@ -407,8 +411,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "kernel": "recurrent step", "achieved": hb["achieved"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": hb["frac"],
-            "traffic": (profiled_traffic(TRAFFIC_PROFILES[(args.config, m["engine"])])
-                        if (args.config, m["engine"]) in TRAFFIC_PROFILES else None),
+            "traffic": hb["traffic"],
             "bytes_per_launch": hb["bytes_per_launch"], "launch_us": m["step_launch_us"],
             "launches_per_layer": max(1, m["step_launches"]),
             "binding": m["binding"],
