@@ -112,6 +112,14 @@ typedef struct {
   int64_t max_length;          /* 0: S.  Otherwise a host-side bound on the sequence lengths (<= S):
                                   only that many steps run, and longer rows are cut to it */
   int32_t engine;              /* rnn_engine hint */
+  int32_t x_bidirectional_y;   /* 0, or 1: X is the Y output of a bidirectional layer of the same layout and
+                                  sequence length, read in place as this layer's input (stacked layers; the
+                                  recognizer of the onegpu docs' CRNN stacks two bidirectional LSTMs).  input
+                                  must then be even, I = 2 H'.  Layout 0: Y [S, 2, B, H'] is read as X
+                                  [S, B, 2H'], element (t, b, k) = Y[t, k / H', b, k % H'] (two pieces of
+                                  H' per row, B*H' elements apart, gathered by the projection; no transpose).
+                                  Layout 1: Y [B, S, 2, H'] already is X [B, S, 2H'] in memory, so 1 changes
+                                  nothing. */
 } rnn_problem_desc;
 
 /* Opaque, immutable after creation; safe to share between threads. */

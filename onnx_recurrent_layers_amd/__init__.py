@@ -44,7 +44,7 @@ class rnn_problem_desc(ctypes.Structure):
         ("input", ctypes.c_int64), ("hidden", ctypes.c_int64), ("clip", ctypes.c_float),
         ("input_forget", ctypes.c_int32), ("linear_before_reset", ctypes.c_int32),
         ("num_activations", ctypes.c_int32), ("activations", rnn_activation * 6),
-        ("max_length", ctypes.c_int64), ("engine", ctypes.c_int32),
+        ("max_length", ctypes.c_int64), ("engine", ctypes.c_int32), ("x_bidirectional_y", ctypes.c_int32),
     ]
 
 
@@ -155,6 +155,7 @@ def make_desc(spec, engine: str = "auto") -> rnn_problem_desc:
         d.activations[i].beta = float(b)
     d.max_length = int(spec.max_length or 0)
     d.engine = ENGINES[engine]
+    d.x_bidirectional_y = int(getattr(spec, "x_bidirectional_y", 0))
     return d
 
 

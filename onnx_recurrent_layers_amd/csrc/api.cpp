@@ -96,6 +96,11 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     return fail(RNN_ERR_ARG, cell, "linear_before_reset: only a GRU takes linear_before_reset");
   if (desc->engine < RNN_ENGINE_AUTO || desc->engine > RNN_ENGINE_PERSISTENT)
     return fail(RNN_ERR_ARG, cell, "engine: unknown value %d", desc->engine);
+  if (desc->x_bidirectional_y != 0 && desc->x_bidirectional_y != 1)
+    return fail(RNN_ERR_ARG, cell, "x_bidirectional_y: must be 0 or 1");
+  if (desc->x_bidirectional_y && desc->input % 2 != 0)
+    return fail(RNN_ERR_SHAPE, cell, "x_bidirectional_y: input must be even (two directions of H'), got %lld",
+                (long long)desc->input);
 
   Problem* p = new (std::nothrow) Problem();
   if (!p) return fail(RNN_ERR_ARG, cell, "out of host memory");
@@ -533,6 +538,11 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
     pa.H = p.H;
     pa.f32_split = p.f32_split_proj;
+    // X as the Y [S,2,B,I/2] of a bidirectional layout-0 layer: rows in two
+    // pieces, the second (B-1)*I/2 elements after the end of the first
+    const bool split_x = p.desc.x_bidirectional_y && p.desc.layout == 0 && p.B > 1;
+    pa.xkh = split_x ? p.I / 2 : p.I;
+    pa.xjump = split_x ? (p.B - 1) * (p.I / 2) : 0;
     // the state setup rides in the same launch (extra workgroups)
     if ((e = launch_projection(pa, sa, p.desc.dtype, s)) != hipSuccess)
       return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));

@@ -109,6 +109,20 @@ __device__ __forceinline__ int64_t y_index(int layout, int S, int D, int B, int 
   return layout == 0 ? ((int64_t(t) * D + d) * B + b) * H + j : ((int64_t(b) * S + t) * D + d) * H + j;
 }
 
+// Element offset in X of row m = t*B + b of the projection's A operand:
+// layout 0 m*K, layout 1 (b*S + t)*K.  A row in two pieces (X is the Y
+// [S,2,B,H'] of a bidirectional layout-0 layer, K = 2H'): it starts at
+// Y[t,0,b,0] = (2tB + b)*H' and its second half at Y[t,1,b,0], B*H'
+// elements after the first; x_col maps element k of the row to its offset
+// from the row start.
+__device__ __forceinline__ int64_t x_row_off(const ProjArgs& a, int64_t m) {
+  const int64_t t = m / a.B, b = m - t * a.B;
+  if (a.layout == 1) return (b * a.S + t) * a.K;
+  if (a.xjump != 0) return (2 * t * a.B + b) * a.xkh;
+  return m * a.K;
+}
+__device__ __forceinline__ int64_t x_col(const ProjArgs& a, int64_t k) { return k + (k >= a.xkh ? a.xjump : 0); }
+
 // Index of a state tensor (initial_h, initial_c, Y_h, Y_c) for direction d,
 // batch row b, unit j: layout 0 [D][B][H], layout 1 [B][D][H].
 __device__ __forceinline__ int64_t state_index(int layout, int D, int B, int H, int d, int b, int j) {

@@ -31,21 +31,19 @@ template <typename T> struct Seg;
 template <> struct Seg<half_t> { typedef f16x8 type; };
 template <> struct Seg<float> { typedef float4 type; };
 
-// Row m of the product (m = t*B + b) -> row of X in its layout.
-__device__ __forceinline__ int64_t x_row(int64_t m, int64_t S, int64_t B, int layout) {
-  if (layout == 0) return m;
-  const int64_t t = m / B, b = m - t * B;
-  return b * S + t;
-}
-
+// The segment of SEG elements at k of a row starting at p (zeros past K);
+// elements at or past kh lie `jump` further on (a row of X in two pieces; W
+// rows pass kh = K).  VEC: whole segments in one load, which the host allows
+// only when no segment straddles kh.
 template <typename T, bool VEC>
-__device__ __forceinline__ typename Seg<T>::type load_seg(const T* p, int64_t k, int64_t K) {
+__device__ __forceinline__ typename Seg<T>::type load_seg(const T* p, int64_t k, int64_t K, int64_t kh,
+                                                          int64_t jump) {
   typedef typename Seg<T>::type V;
   constexpr int SEG = ProjCfg<T>::SEG;
-  if (VEC && k + SEG <= K) return *reinterpret_cast<const V*>(p + k);
+  if (VEC && k + SEG <= K) return *reinterpret_cast<const V*>(p + k + (k >= kh ? jump : 0));
   V v;
 #pragma unroll
-  for (int z = 0; z < SEG; ++z) v[z] = (k + z < K) ? p[k + z] : T(0.f);
+  for (int z = 0; z < SEG; ++z) v[z] = (k + z < K) ? p[k + z + (k + z >= kh ? jump : 0)] : T(0.f);
   return v;
 }
 
@@ -85,7 +83,7 @@ __global__ __launch_bounds__(256) void projection_kernel(ProjArgs a, SetupArgs s
   for (int i = 0; i < APER; ++i) {
     const int q = tid + i * 256, r = q / SEGROW;
     ak[i] = (q % SEGROW) * SEG;
-    ap[i] = (m0 + r < a.M) ? X + x_row(m0 + r, a.S, a.B, a.layout) * a.K : nullptr;
+    ap[i] = (m0 + r < a.M) ? X + x_row_off(a, m0 + r) : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < BPER; ++i) {
@@ -98,12 +96,12 @@ __global__ __launch_bounds__(256) void projection_kernel(ProjArgs a, SetupArgs s
 #pragma unroll
     for (int i = 0; i < APER; ++i) {
       V z{};
-      ra[i] = ap[i] ? load_seg<T, VEC>(ap[i], k0 + ak[i], a.K) : z;
+      ra[i] = ap[i] ? load_seg<T, VEC>(ap[i], k0 + ak[i], a.K, a.xkh, a.xjump) : z;
     }
 #pragma unroll
     for (int i = 0; i < BPER; ++i) {
       V z{};
-      rb[i] = bp[i] ? load_seg<T, VEC>(bp[i], k0 + bk[i], a.K) : z;
+      rb[i] = bp[i] ? load_seg<T, VEC>(bp[i], k0 + bk[i], a.K, a.K, 0) : z;
     }
   };
   auto stash = [&](int buf) {
@@ -243,7 +241,7 @@ __global__ __launch_bounds__(256) void projection_bf16x3_kernel(ProjArgs a, Setu
   for (int i = 0; i < APER; ++i) {
     const int q = tid + i * 256, r = q / SEGROW;
     ak[i] = (q % SEGROW) * SEG;
-    ap[i] = (m0 + r < a.M) ? X + x_row(m0 + r, a.S, a.B, a.layout) * a.K : nullptr;
+    ap[i] = (m0 + r < a.M) ? X + x_row_off(a, m0 + r) : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < BPER; ++i) {
@@ -254,9 +252,10 @@ __global__ __launch_bounds__(256) void projection_bf16x3_kernel(ProjArgs a, Setu
   float4 ra[APER], rb[BPER];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < APER; ++i) ra[i] = ap[i] ? load_seg<float, VEC>(ap[i], k0 + ak[i], a.K) : float4{};
+    for (int i = 0; i < APER; ++i)
+      ra[i] = ap[i] ? load_seg<float, VEC>(ap[i], k0 + ak[i], a.K, a.xkh, a.xjump) : float4{};
 #pragma unroll
-    for (int i = 0; i < BPER; ++i) rb[i] = bp[i] ? load_seg<float, VEC>(bp[i], k0 + bk[i], a.K) : float4{};
+    for (int i = 0; i < BPER; ++i) rb[i] = bp[i] ? load_seg<float, VEC>(bp[i], k0 + bk[i], a.K, a.K, 0) : float4{};
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -381,20 +380,29 @@ __global__ __launch_bounds__(256) void projection_small_kernel(ProjArgs a, Setup
   // in both operands, so that such a product is exactly zero; a row past M or
   // N feeds only outputs that are dropped.  The mask is a bit mask, not a
   // select, which keeps the compiler from moving the loads into branches.
-  const T* ap = X + x_row(m0 + r32 < a.M ? m0 + r32 : a.M - 1, a.S, a.B, a.layout) * a.K;
+  const T* ap = X + x_row_off(a, m0 + r32 < a.M ? m0 + r32 : a.M - 1);
   const T* bp = W + (n0 + r32 < a.N ? n0 + r32 : a.N - 1) * a.K;
-  auto seg = [&](const T* p, int64_t k) {
-    if constexpr (VEC) {  // K is a whole number of segments
-      return *reinterpret_cast<const u32x4*>(p + (k < a.K ? k : 0));
+  // (rows of X in two pieces: elements at or past kh lie `jump` further on;
+  // W passes kh = K)
+  auto seg = [&](const T* p, int64_t k, int64_t kh, int64_t jump) {
+    if constexpr (VEC) {  // K is a whole number of segments, none straddles kh
+      const int64_t kk = k < a.K ? k : 0;
+      return *reinterpret_cast<const u32x4*>(p + kk + (kk >= kh ? jump : 0));
     } else if constexpr (sizeof(T) == 4) {
       u32x4 u;
 #pragma unroll
-      for (int z = 0; z < SEG; ++z) u[z] = reinterpret_cast<const unsigned*>(p)[k + z < a.K ? k + z : a.K - 1];
+      for (int z = 0; z < SEG; ++z) {
+        const int64_t kk = k + z < a.K ? k + z : a.K - 1;
+        u[z] = reinterpret_cast<const unsigned*>(p)[kk + (kk >= kh ? jump : 0)];
+      }
       return u;
     } else {
       u16x8 u;
 #pragma unroll
-      for (int z = 0; z < SEG; ++z) u[z] = reinterpret_cast<const unsigned short*>(p)[k + z < a.K ? k + z : a.K - 1];
+      for (int z = 0; z < SEG; ++z) {
+        const int64_t kk = k + z < a.K ? k + z : a.K - 1;
+        u[z] = reinterpret_cast<const unsigned short*>(p)[kk + (kk >= kh ? jump : 0)];
+      }
       return __builtin_bit_cast(u32x4, u);
     }
   };
@@ -428,8 +436,8 @@ __global__ __launch_bounds__(256) void projection_small_kernel(ProjArgs a, Setup
     u32x4 ra[NSEG], rb[NSEG];
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
-      ra[i] = seg(ap, k0 + i * SEG);
-      rb[i] = seg(bp, k0 + i * SEG);
+      ra[i] = seg(ap, k0 + i * SEG, a.xkh, a.xjump);
+      rb[i] = seg(bp, k0 + i * SEG, a.K, 0);
     }
     // keep the scheduler from moving each load down to its use
     __builtin_amdgcn_sched_barrier(0);
@@ -470,8 +478,8 @@ static hipError_t launch_small(const ProjArgs& a, const SetupArgs& sa, int setup
   const int64_t gemm = (a.M > 0 && a.N > 0) ? mt * nt * a.D : 0;
   if (gemm + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int seg = ProjCfg<T>::SEG;
-  const bool vec = a.K % seg == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+  const bool vec = a.K % seg == 0 && a.xkh % seg == 0 && a.xjump % seg == 0 &&
+                   reinterpret_cast<uintptr_t>(a.X) % 16 == 0 && reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
   const dim3 grid(unsigned(gemm + setup_blocks));
   if (vec)
     hipLaunchKernelGGL((projection_small_kernel<T, true>), grid, dim3(256), 0, s, a, sa, int(gemm));
@@ -485,8 +493,8 @@ static hipError_t launch_bf16x3(const ProjArgs& a, const SetupArgs& sa, int setu
   const int64_t mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
   const int64_t gemm = (a.M > 0 && a.N > 0) ? mt * nt * a.D : 0;
   if (gemm + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const bool vec = a.K % 4 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+  const bool vec = a.K % 4 == 0 && a.xkh % 4 == 0 && a.xjump % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.X) % 16 == 0 && reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
   const dim3 grid(unsigned(gemm + setup_blocks));
   if (vec)
     hipLaunchKernelGGL((projection_bf16x3_kernel<BM, BN, true>), grid, dim3(256), 0, s, a, sa, int(gemm));
@@ -501,8 +509,8 @@ static hipError_t launch_tile(const ProjArgs& a, const SetupArgs& sa, int setup_
   const int64_t gemm = (a.M > 0 && a.N > 0) ? mt * nt * a.D : 0;
   if (gemm + setup_blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int seg = ProjCfg<T>::SEG;
-  const bool vec = a.K % seg == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+  const bool vec = a.K % seg == 0 && a.xkh % seg == 0 && a.xjump % seg == 0 &&
+                   reinterpret_cast<uintptr_t>(a.X) % 16 == 0 && reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
   const dim3 grid(unsigned(gemm + setup_blocks));
   if (vec)
     hipLaunchKernelGGL((projection_kernel<T, BM, BN, true>), grid, dim3(256), 0, s, a, sa, int(gemm));

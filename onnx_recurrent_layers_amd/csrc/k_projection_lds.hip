@@ -121,12 +121,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
     const int row = (wave * kLoads + i) * 16 + (lane >> 2);
     seg[i] = (lane & 3) ^ ((row >> 2) & 3);
     const int64_t m = m0 + row, n = n0 + row;
-    int64_t xr = m;
-    if (a.layout == 1 && m < a.M) {
-      const int64_t tt = m / a.B;
-      xr = (m - tt * a.B) * a.S + tt;
-    }
-    xrow[i] = m < a.M ? unsigned(xr * K * ES) : kOOB;
+    xrow[i] = m < a.M ? unsigned(x_row_off(a, m) * ES) : kOOB;
     wrow[i] = n < a.N ? unsigned(n * K * ES) : kOOB;
   }
   auto fetch = [&](int kc, unsigned char* sa_, unsigned char* sb_) {
@@ -134,7 +129,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
     for (int i = 0; i < kLoads; ++i) {
       const int k = kc * KC + seg[i] * SEGE;
       // a row outside the matrix starts at the out-of-range marker, so row + k stays out of range
-      const unsigned ox = k < K ? xrow[i] + unsigned(k) * unsigned(ES) : kOOB;
+      const unsigned ox = k < K ? xrow[i] + unsigned(x_col(a, k)) * unsigned(ES) : kOOB;
       const unsigned ow = k < K ? wrow[i] + unsigned(k) * unsigned(ES) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, RNN_LDS_PTR(sa_ + (wave * kLoads + i) * 1024), 16, ox, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, RNN_LDS_PTR(sb_ + (wave * kLoads + i) * 1024), 16, ow, 0, 0, 0);
@@ -240,7 +235,9 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
 hipError_t launch_projection_lds(const ProjArgs& a, const SetupArgs& sa, int setup_blocks, int dtype,
                                  hipStream_t s) {
   const int es = dtype == RNN_DTYPE_F32 ? 4 : 2;
-  if (a.K % (16 / es) != 0 || reinterpret_cast<uintptr_t>(a.X) % 16 != 0 || reinterpret_cast<uintptr_t>(a.W) % 16 != 0)
+  const int sege = 16 / es;
+  if (a.K % sege != 0 || a.xkh % sege != 0 || a.xjump % sege != 0 || reinterpret_cast<uintptr_t>(a.X) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(a.W) % 16 != 0)
     return hipErrorNotSupported;
   if (a.S * a.B * a.K * es >= int64_t(kOOB) || a.N * a.K * es >= int64_t(kOOB)) return hipErrorNotSupported;
   TileMap tm{};

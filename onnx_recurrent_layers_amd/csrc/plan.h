@@ -115,6 +115,10 @@ struct ProjArgs {
   int skip_block;     // gate block of H columns not needed (input_forget: f), or -1
   int64_t H;
   int f32_split;      // f32 tensors: products on the bf16 matrix cores as three split products
+  // X rows in two pieces (the Y [S,2,B,K/2] of a bidirectional layout-0 layer
+  // read as X): elements k >= xkh of a row lie xjump elements further on.
+  // Otherwise xkh = K and xjump = 0.
+  int64_t xkh, xjump;
 };
 
 struct SetupArgs {

@@ -50,6 +50,9 @@ class LayerSpec:
     init_c: bool = False
     lens: bool = False
     outputs: Tuple[str, ...] = ("Y", "Y_h", "Y_c")
+    # X is the Y of a bidirectional layer of the same layout, read in place
+    # (layout 0: [S, 2, B, input/2] read as [S, B, input])
+    x_bidirectional_y: int = 0
 
     @property
     def num_directions(self) -> int:

@@ -66,6 +66,7 @@ def create_err(desc):
     ("LSTM", "num_activations", 2, rl.RNN_ERR_ARG, "activations"),
     ("LSTM", "clip", float("nan"), rl.RNN_ERR_ARG, "clip"),
     ("RNN", "engine", 9, rl.RNN_ERR_ARG, "engine"),
+    ("GRU", "x_bidirectional_y", 2, rl.RNN_ERR_ARG, "x_bidirectional_y"),
 ])
 def test_create_rejects(lib, cell, field, value, code, needle):
     d = rl.make_desc(spec(cell))
@@ -74,6 +75,17 @@ def test_create_rejects(lib, cell, field, value, code, needle):
     assert rc == code, (rc, msg)
     assert needle in msg and msg.startswith(cell), msg
     assert h is None
+
+
+def test_bidirectional_y_input_must_be_even(lib):
+    d = rl.make_desc(spec("LSTM", input=5))
+    d.x_bidirectional_y = 1
+    rc, msg, h = create_err(d)
+    assert rc == rl.RNN_ERR_SHAPE and "input must be even" in msg and msg.startswith("LSTM"), msg
+    d.input = 6
+    rc, msg, h = create_err(d)
+    assert rc == rl.RNN_OK, msg
+    rl.rnn_problem_destroy(h)
 
 
 def test_bad_activation_kind(lib):

@@ -758,6 +758,68 @@ def test_stacked_layers_without_transpose():
         compare(s2, {k: v.cpu().numpy() for k, v in got.items()}, ref, what=f"stacked layer 2 {engine}")
 
 
+# Two stacked bidirectional layout-0 layers (the recognizer's stack): the
+# second reads the first's Y [S, 2, B, H'] in place as its X [S, B, 2H'], each
+# row gathered by the projection from two pieces (x_bidirectional_y = 1).
+# Cases reach every projection kernel (small layers, 64/128 tiles, the
+# 256x256 direct-to-LDS tiles in f16 and in bf16-split f32, the
+# register-staged bf16 split kernel) and the element-wise path (H' not a
+# whole number of 16-byte segments).  Checked against the oracle fed the
+# first layer's Y transposed on the host, and bit for bit against the same
+# second layer run on that transposed copy.
+STACK0 = [("f32", 48, 5, {}), ("f16", 48, 5, {}), ("f32", 37, 5, {}), ("f16", 37, 3, {}),
+          ("f16", 64, 8, {"RNN_SMALL_PROJECTION": "0"}), ("f32", 36, 7, {"RNN_SMALL_PROJECTION": "0"}),
+          ("f16", 64, 8, {"RNN_PROJ_LDS_MIN_TILES": "1"}),
+          ("f32", 64, 8, {"RNN_F32_SPLIT": "1", "RNN_PROJ_LDS_MIN_TILES": "1"}),
+          ("f32", 64, 8, {"RNN_F32_SPLIT": "1", "RNN_PROJ_LDS_MIN_TILES": "1000000000"}),
+          ("f32", 40, 1, {})]
+
+
+@pytest.mark.parametrize("dtype,H1,B,env", STACK0, ids=[f"{d}-H{h}-B{b}-{'-'.join(e) or 'auto'}"
+                                                       for d, h, b, e in STACK0])
+def test_stacked_bidirectional_layout0(dtype, H1, B, env, monkeypatch):
+    import torch
+    import onnx_recurrent_layers_amd as rl
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    S = 11
+    s1 = LayerSpec("LSTM", seq=S, batch=B, input=20, hidden=H1, direction="bidirectional", layout=0, dtype=dtype,
+                   init_h=True, init_c=True, lens=True, outputs=("Y",))
+    in1 = make_inputs(s1, 95, Dists(sequence_lens=("I", 1, S)))
+    y1 = rl.run(s1, in1, outputs=("Y",))["Y"]
+    assert tuple(y1.shape) == (S, 2, B, H1)
+    compare(s1, {"Y": y1.cpu().numpy()}, oracle.run(s1, in1, outputs=("Y",)), what="stacked layer 1")
+    xt = y1.permute(0, 2, 1, 3).contiguous().view(S, B, 2 * H1)   # the same values as one X row each
+    for cell in ("LSTM", "GRU"):
+        s2 = LayerSpec(cell, seq=S, batch=B, input=2 * H1, hidden=24, direction="bidirectional", layout=0,
+                       dtype=dtype, init_h=True, init_c=cell == "LSTM", lens=True, outputs=("Y", "Y_h"))
+        in2 = make_inputs(s2, 96)
+        in2["sequence_lens"] = in1["sequence_lens"]
+        dev = rl.to_device({k: v for k, v in in2.items() if k != "X"})
+        note(f"case stacked layout 0 {cell} {dtype} H'={H1} B={B} {env}")
+        got = rl.run(s2.replace(x_bidirectional_y=1), {**dev, "X": y1}, outputs=s2.outputs)   # Y read in place
+        ref = oracle.run(s2, {**in2, "X": xt.cpu().numpy()}, outputs=s2.outputs)
+        compare(s2, {k: v.cpu().numpy() for k, v in got.items()}, ref, what=f"stacked layer 2 {cell}")
+        plain = rl.run(s2, {**dev, "X": xt}, outputs=s2.outputs)
+        for n in got:
+            assert torch.equal(got[n].view(torch.int16 if dtype == "f16" else torch.int32),
+                               plain[n].view(torch.int16 if dtype == "f16" else torch.int32)), f"{cell} {n}: bits differ"
+
+
+def test_bidirectional_y_flag_is_a_no_op_in_layout_1():
+    """Layout 1: Y [B, S, 2, H'] is X [B, S, 2H'] already; x_bidirectional_y = 1
+    reads it exactly as a plain X."""
+    import torch
+    import onnx_recurrent_layers_amd as rl
+    s2 = LayerSpec("GRU", seq=6, batch=4, input=30, hidden=16, direction="bidirectional", layout=1, dtype="f32",
+                   init_h=True, outputs=("Y", "Y_h"))
+    inp = make_inputs(s2, 97)
+    a = rl.run(s2.replace(x_bidirectional_y=1), inp, outputs=s2.outputs)
+    b = rl.run(s2, inp, outputs=s2.outputs)
+    for n in a:
+        assert torch.equal(a[n].view(torch.int32), b[n].view(torch.int32)), n
+
+
 @pytest.mark.parametrize("cell,engine", [("LSTM", "persistent"), ("GRU", "launch"), ("RNN", "persistent"),
                                          ("LSTM", "launch")])
 def test_streaming_continuation(cell, engine):
