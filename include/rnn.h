@@ -91,7 +91,7 @@ typedef struct {
 typedef enum {
   RNN_ENGINE_AUTO = 0,
   RNN_ENGINE_LAUNCH = 1,      /* one kernel launch per step (two for GRU linear_before_reset=0) */
-  RNN_ENGINE_PERSISTENT = 2   /* one launch for all steps (small batches; the matrix-core step for batches of 16 and more) */
+  RNN_ENGINE_PERSISTENT = 2   /* one launch for all steps (batches up to eight; the matrix-core step above eight) */
 } rnn_engine;
 
 /* Layer description (the page's RecurrentProblem plus ONNX attributes). */
@@ -153,9 +153,9 @@ typedef struct {
  *
  * Limits (RNN_ERR_UNSUPPORTED): hidden above 2^24; batch or seq above 2^30;
  * engine = RNN_ENGINE_PERSISTENT on a shape that neither persistent form
- * takes (batches of 9 to 15 never; the vector form needs a batch of at most
- * 8 whose units fit the workgroups' LDS; the matrix-core form needs a batch
- * of 16 or more whose tiles fit the chip at once).  RNN_ENGINE_AUTO never
+ * takes (the vector form needs a batch of at most 8 whose units fit the
+ * workgroups' LDS; the matrix-core form a batch above 8, rows of whole
+ * 16-byte segments and tiles that fit the chip at once).  RNN_ENGINE_AUTO never
  * fails for that reason; rnn_problem_plan shows the engine it chose.  A
  * tensor, Y or the projection scratch above 2^52 bytes is RNN_ERR_SHAPE. */
 int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** out);

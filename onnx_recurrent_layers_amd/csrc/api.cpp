@@ -180,17 +180,20 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     if (const char* e = std::getenv("RNN_F32_SPLIT")) want = std::atoi(e) != 0;
     p->f32_split_step = want && step_dma_supported(t, 2);
   }
-  // Batches of 16 and more: the matrix-core step, in one persistent launch
-  // when its tiles fit the chip (else one launch per step).  The automatic
-  // choice takes the persistent launch only for f16 layers with the default
-  // activations (split h): there it measured faster than one launch per step
-  // (LSTM 256/64/1024/1024: 2.41 against 2.53 ms of steps), while for f32
-  // layers it measured slower (RNN 1024/256/1024/2048 in bf16 split mode:
-  // 35 against 33 ms).
+  // Batches above eight: the matrix-core step, in one persistent launch when
+  // its tiles fit the chip (else one launch per step).  The automatic choice
+  // takes the persistent launch for f16 layers with the default activations
+  // (split h), where it measured faster than one launch per step (LSTM
+  // 256/64/1024/1024: 2.41 against 2.53 ms of steps), and for layers whose
+  // per-step product is below 2^28 flops, whose steps are too short to cover
+  // a launch each; large f32 layers measured slower persistent (RNN
+  // 1024/256/1024/2048 in bf16 split mode: 35 against 33 ms).
   int mfma_tiles = 0;
   const bool pers_mfma_ok =
       !pers_ok && p->S > 0 && p->steps > 0 && p->B > 0 && mfma_persistent_supported(*p, &mfma_tiles);
-  const bool pers_mfma_auto = pers_mfma_ok && desc->dtype == RNN_DTYPE_F16 && p->def_acts;
+  const double step_flops = 2.0 * double(p->D) * double(p->B) * double(GH) * double(p->H);
+  const bool pers_mfma_auto =
+      pers_mfma_ok && ((desc->dtype == RNN_DTYPE_F16 && p->def_acts) || step_flops < 268435456.0);
   if (engine == RNN_ENGINE_AUTO)
     engine = (pers_ok || pers_mfma_auto) ? RNN_ENGINE_PERSISTENT : RNN_ENGINE_LAUNCH;
   if (engine == RNN_ENGINE_PERSISTENT && !pers_ok && !pers_mfma_ok)
@@ -559,7 +562,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
       if ((e = launch_step_persistent(a, p, io, s)) != hipSuccess)
         return fail(RNN_ERR_HIP, cell, "persistent step launch: %s", hipGetErrorString(e));
     } else {
-      // batches of 16 and more: the product of each step on the matrix cores
+      // batches above eight: the product of each step on the matrix cores
       const bool mfma = mfma_step_supported(p);
       if (p.f32_split_step && (e = launch_split_r(R, rsplit, int64_t(p.D) * p.G * p.H * p.H, s)) != hipSuccess)
         return fail(RNN_ERR_HIP, cell, "R split launch: %s", hipGetErrorString(e));

@@ -447,7 +447,9 @@ void mfma_tile(int B, int H, int D, int Gp, int* bm, int* uj) {
   }
 }
 
-bool mfma_step_supported(const Problem& p) { return p.B >= 16; }
+// Batches above eight (the small-batch engine takes eight and fewer): 16-row
+// blocks, the rows past the batch read as zeros and their outputs dropped.
+bool mfma_step_supported(const Problem& p) { return p.B >= 9; }
 
 template <typename T, int BM>
 static hipError_t launch_bm(const MfmaStepArgs& m, int H, int B, int D, hipStream_t s) {

@@ -53,10 +53,10 @@ struct Problem {
   int pers_blocks = 0;       // workgroups of the persistent launch
   int pers_units = 0;        // units per workgroup
   int pers_wg_per_dir = 0;
-  // the persistent engine in its matrix-core form (batches of 16 and more)
+  // the persistent engine in its matrix-core form (batches above eight)
   bool pers_mfma = false;
   // tile of the matrix-core step (batch rows, units), fixed when the problem
-  // is created (batches of 16 and more)
+  // is created (batches above eight)
   int mfma_bm = 16, mfma_uj = 16;
   // f32 tensors: the projection on the bf16 matrix cores (three split
   // products) instead of the f32 matrix cores

@@ -184,6 +184,23 @@ CONFIGS = {
         dists=Dists(W=("U", -0.02, 0.02), R=("U", -0.02, 0.02), B=("U", -0.05, 0.05)),
         seed=5,
         name="biRNN S1024 B256 I1024 H2048 f32 L0 Relu/ScaledTanh"),
+    # The C2 layer at batch 8 (the small-batch engine's largest) and batch 12
+    # (the matrix-core step with one 16-row block): the cost of a batch
+    # above eight.
+    "C2B8": dict(
+        spec=LayerSpec("LSTM", seq=80, batch=8, input=256, hidden=256, direction="bidirectional",
+                       dtype="f32", init_h=True, init_c=True, outputs=("Y", "Y_h")),
+        dists=Dists(W=("U", -1 / 16, 1 / 16), R=("U", -1 / 16, 1 / 16), B=("U", -0.1, 0.1),
+                    initial_h=("N", 0.0, 0.5), initial_c=("N", 0.0, 0.5)),
+        seed=2,
+        name="biLSTM S80 B8 I256 H256 f32 L0"),
+    "C2B12": dict(
+        spec=LayerSpec("LSTM", seq=80, batch=12, input=256, hidden=256, direction="bidirectional",
+                       dtype="f32", init_h=True, init_c=True, outputs=("Y", "Y_h")),
+        dists=Dists(W=("U", -1 / 16, 1 / 16), R=("U", -1 / 16, 1 / 16), B=("U", -0.1, 0.1),
+                    initial_h=("N", 0.0, 0.5), initial_c=("N", 0.0, 0.5)),
+        seed=2,
+        name="biLSTM S80 B12 I256 H256 f32 L0"),
     # The text-line recognizer shapes the "Recurrent layers" page tests
     # ("Tolerance and evidence"): bidirectional LSTMs of sequence 80 and 48,
     # batch 1 and 8, input 256 and 192, hidden 256 and 96.  The page gives

@@ -254,11 +254,28 @@ def test_sizes_at_the_limits(lib, cell, kw):
     rl.rnn_problem_destroy(h)
 
 
-@pytest.mark.parametrize("kw", [dict(batch=9, hidden=40), dict(batch=15, hidden=40), dict(batch=3, hidden=5000),
+@pytest.mark.parametrize("kw", [dict(batch=9, hidden=41), dict(batch=15, hidden=39), dict(batch=3, hidden=5000),
                                 dict(batch=40, hidden=4000)])
 def test_persistent_engine_refuses_other_shapes(lib, kw):
     rc, msg, _ = create_err(rl.make_desc(spec("LSTM", **kw), "persistent"))
     assert rc == rl.RNN_ERR_UNSUPPORTED and "persistent engine" in msg, (rc, msg)
     h = rl.rnn_problem_create(rl.make_desc(spec("LSTM", **kw), "auto"))   # the automatic choice takes it
+    assert rl.rnn_problem_plan(h).engine == rl.ENGINES["launch"]
+    rl.rnn_problem_destroy(h)
+
+
+@pytest.mark.parametrize("batch", [9, 12, 15, 16])
+def test_batches_above_eight_take_the_matrix_core_step(lib, batch):
+    """Batches above eight run on the matrix-core step (16-row blocks); a small
+    f32 layer (a per-step product far below 2^28 flops) takes its persistent
+    form automatically, a large one keeps one launch per step."""
+    s = spec("LSTM", batch=batch, hidden=256, input=256, seq=80, direction="bidirectional")
+    h = rl.rnn_problem_create(rl.make_desc(s, "auto"))
+    info = rl.rnn_problem_plan(h)
+    assert info.engine == rl.ENGINES["persistent"] and info.step_blocks > 0 and info.step_launches == 1
+    assert rl.PRODUCTS[info.step_products] == "f32 matrix cores"
+    rl.rnn_problem_destroy(h)
+    s = spec("RNN", batch=batch, hidden=4096, input=64, seq=4, direction="bidirectional")
+    h = rl.rnn_problem_create(rl.make_desc(s, "auto"))
     assert rl.rnn_problem_plan(h).engine == rl.ENGINES["launch"]
     rl.rnn_problem_destroy(h)

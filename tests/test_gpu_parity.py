@@ -658,6 +658,28 @@ def test_f16_outputs_round_to_nearest_even(engine, B, layout):
                                f"{have[tuple(bad[0])]:#06x}, nearest-even is {want[tuple(bad[0])]:#06x}")
 
 
+# Batches of 9 to 15 run on the matrix-core step with one 16-row block whose
+# rows past the batch read as zeros: every cell and GRU form, both dtypes,
+# lengths with 0, peepholes, clip, input_forget; the automatic choice (the
+# persistent form for these small layers) and one launch per step.
+B9 = [(c, o, dt, b) for c, o in (("LSTM", 0), ("LSTM", 1), ("GRU", 0), ("GRU", 1), ("RNN", 0))
+      for dt in ("f32", "f16") for b in (9, 15)]
+
+
+@pytest.mark.parametrize("cell,opt,dtype,B", B9, ids=[f"{c}-{o}-{d}-B{b}" for c, o, d, b in B9])
+def test_batches_nine_to_fifteen(cell, opt, dtype, B):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=9, batch=B, input=40, hidden=64, direction="bidirectional", layout=opt, dtype=dtype,
+                     linear_before_reset=opt if cell == "GRU" else 0, input_forget=opt if cell == "LSTM" else 0,
+                     init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM", clip=2.5,
+                     outputs=("Y", "Y_h", "Y_c"))
+    inp = make_inputs(spec, 113, Dists(sequence_lens=("I", 0, 9), W=("U", -0.2, 0.2), R=("U", -0.2, 0.2)))
+    layer = rl.Layer(spec, engine="auto", device="cuda:0")
+    assert rl.PRODUCTS[layer.plan.step_products] != "f32 vector ALU"
+    for engine in ("auto", "launch"):
+        check(spec, inp, engine=engine, what=f"B{B} {cell} opt{opt} {dtype} {engine}")
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 def test_batch_above_eight_and_hidden_not_dividing(engine):
     for cell, H in (("LSTM", 65), ("GRU", 127), ("RNN", 129)):
