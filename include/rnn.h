@@ -120,6 +120,15 @@ typedef struct {
                                   H' per row, B*H' elements apart, gathered by the projection; no transpose).
                                   Layout 1: Y [B, S, 2, H'] already is X [B, S, 2H'] in memory, so 1 changes
                                   nothing. */
+  int64_t xw_chunk_steps;      /* the input projection in chunks of this many steps, through a ring of two
+                                  chunks in the projection scratch (the page's "Scratch": XwLength grows with
+                                  the layer), each chunk's projection enqueued ahead of its steps and
+                                  overlapping the steps of the chunk before: 0 lets the library choose (one
+                                  chunk, unless the whole projection exceeds 512 MiB); n > 0 asks for chunks
+                                  of n steps.  Only the per-step engine (RNN_ENGINE_LAUNCH) runs in chunks;
+                                  the persistent engines read every step's projection in their one launch
+                                  and always take one chunk.  rnn_scratch_size and rnn_problem_plan report
+                                  the outcome.  >= 0. */
 } rnn_problem_desc;
 
 /* Opaque, immutable after creation; safe to share between threads. */
@@ -164,9 +173,13 @@ int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** out);
 void rnn_problem_destroy(rnn_problem* problem);
 
 /* Scratch the caller must supply to rnn_encode (the page's "Scratch"):
- *   *xw_bytes    = 4 * D * S * B * G * H: the f32 input projection, laid out
- *                  time-major [D][S][B][G*H] (row t*B+b of direction d holds
- *                  X[t,b,:] . W[d]^T);
+ *   *xw_bytes    = 4 * slots * D * C * B * G * H: the f32 input projection
+ *                  in `slots` slots of C steps each (one slot of C = the steps
+ *                  run, max_length or S, unless the projection runs in chunks:
+ *                  then two slots of C = the chunk's steps), laid out
+ *                  step-major [slot][D][C][B][G*H]: row b of step s of
+ *                  direction d holds X[t,b,:] . W[d]^T for the time t that
+ *                  step reads (s forward, len_b - 1 - s backward);
  *   *state_bytes = the f32 hidden state (two slots of [D][B][H]), the f32
  *                  cell state, the GRU two-pass buffers, and for the
  *                  persistent engine its exchange words and status words.
@@ -238,6 +251,8 @@ typedef struct {
   int32_t step_launches;   /* launches of the recurrent-step kernel per rnn_encode */
   int32_t proj_products;   /* rnn_products of the input projection */
   int32_t step_products;   /* rnn_products of the recurrent products (R * h) */
+  int32_t xw_chunk_steps;  /* steps per chunk of the projection (the steps run when it is one chunk) */
+  int32_t xw_slots;        /* 1, or 2 (a ring of chunks) */
 } rnn_plan_info;
 int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info);
 

@@ -45,6 +45,7 @@ class rnn_problem_desc(ctypes.Structure):
         ("input_forget", ctypes.c_int32), ("linear_before_reset", ctypes.c_int32),
         ("num_activations", ctypes.c_int32), ("activations", rnn_activation * 6),
         ("max_length", ctypes.c_int64), ("engine", ctypes.c_int32), ("x_bidirectional_y", ctypes.c_int32),
+        ("xw_chunk_steps", ctypes.c_int64),
     ]
 
 
@@ -67,7 +68,8 @@ class rnn_run_status(ctypes.Structure):
 class rnn_plan_info(ctypes.Structure):
     _fields_ = [("engine", ctypes.c_int32), ("steps", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("step_blocks", ctypes.c_int32), ("step_launches", ctypes.c_int32),
-                ("proj_products", ctypes.c_int32), ("step_products", ctypes.c_int32)]
+                ("proj_products", ctypes.c_int32), ("step_products", ctypes.c_int32),
+                ("xw_chunk_steps", ctypes.c_int32), ("xw_slots", ctypes.c_int32)]
 
 
 # rnn_products: which arithmetic units carry a stage's products
@@ -156,6 +158,7 @@ def make_desc(spec, engine: str = "auto") -> rnn_problem_desc:
     d.max_length = int(spec.max_length or 0)
     d.engine = ENGINES[engine]
     d.x_bidirectional_y = int(getattr(spec, "x_bidirectional_y", 0))
+    d.xw_chunk_steps = int(getattr(spec, "xw_chunk_steps", 0))
     return d
 
 

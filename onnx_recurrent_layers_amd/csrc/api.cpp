@@ -5,6 +5,7 @@
 //
 // Every check runs in 64-bit checked arithmetic before anything is enqueued
 // (the page's "Scratch" paragraph); messages name the cell and the argument.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -96,6 +97,8 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     return fail(RNN_ERR_ARG, cell, "linear_before_reset: only a GRU takes linear_before_reset");
   if (desc->engine < RNN_ENGINE_AUTO || desc->engine > RNN_ENGINE_PERSISTENT)
     return fail(RNN_ERR_ARG, cell, "engine: unknown value %d", desc->engine);
+  if (desc->xw_chunk_steps < 0)
+    return fail(RNN_ERR_SHAPE, cell, "xw_chunk_steps: negative (%lld)", (long long)desc->xw_chunk_steps);
   if (desc->x_bidirectional_y != 0 && desc->x_bidirectional_y != 1)
     return fail(RNN_ERR_ARG, cell, "x_bidirectional_y: must be 0 or 1");
   if (desc->x_bidirectional_y && desc->input % 2 != 0)
@@ -152,7 +155,6 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
   int64_t xw;
   if (!mul4(p->D, p->S, p->B, GH, &xw) || !mul_ok(xw, 4, &xw) || xw > kMaxBytes)
     return bad(RNN_ERR_SHAPE, "xw scratch: size overflows");
-  p->xw_bytes = (p->S > 0 && p->B > 0) ? size_t(xw) : 0;
   int64_t dbh;
   if (!mul3(p->D, p->B, p->H, &dbh) || dbh > kMaxBytes / 8) return bad(RNN_ERR_SHAPE, "state: size overflows");
   // The matrix-core step's tile, once: every launch of this problem uses it
@@ -223,6 +225,27 @@ extern "C" int rnn_problem_create(const rnn_problem_desc* desc, rnn_problem** ou
     const double flops = 2.0 * double(p->D) * double(p->S) * double(p->B) * double(GH) * double(p->I);
     p->f32_split_proj = flops >= 4294967296.0;
     if (const char* e = std::getenv("RNN_F32_SPLIT")) p->f32_split_proj = std::atoi(e) != 0;
+  }
+
+  // The projection scratch, step-major.  The per-step engine may run the
+  // projection in chunks through a ring of two slots: at the caller's
+  // request, or when the whole projection would exceed 512 MiB (then slots
+  // of 256 MiB, which keeps each chunk's projection in whole 256x256 tiles
+  // for the large layers that reach this size).  The persistent engines read
+  // every step's projection in their one launch: one slot of every step.
+  {
+    const int64_t per_step = int64_t(p->D) * p->B * GH * 4;   // bytes of one step of every direction
+    int64_t tc = p->steps;
+    if (engine == RNN_ENGINE_LAUNCH && p->steps > 0 && per_step > 0) {
+      if (desc->xw_chunk_steps > 0) {
+        tc = std::min<int64_t>(desc->xw_chunk_steps, p->steps);
+      } else if (p->steps * per_step > (int64_t(512) << 20)) {
+        tc = std::max<int64_t>(1, (int64_t(256) << 20) / per_step);
+      }
+    }
+    p->xw_tc = std::max<int64_t>(tc, 1);
+    p->xw_slots = tc < p->steps ? 2 : 1;
+    p->xw_bytes = (p->S > 0 && p->B > 0 && p->steps > 0) ? size_t(p->xw_slots) * size_t(p->xw_tc) * size_t(per_step) : 0;
   }
 
   StateLayout& st = p->st;
@@ -312,6 +335,7 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
     n += 1;                        // projection with the state setup (or the setup alone when Seq = 0); the
                                    // steps and the setup write the outputs
     if (p->S > 0) n += step_launch_count(*p);
+    if (p->S > 0 && p->steps > 0) n += int((p->steps + p->xw_tc - 1) / p->xw_tc) - 1;   // the later chunks' projections
     if (p->S > 0 && p->steps > 0 && p->engine == RNN_ENGINE_PERSISTENT) n += 1;   // the fallback kernel
     if (p->S > 0 && p->f32_split_step) n += 1;   // R split into bf16 planes
   }
@@ -332,6 +356,8 @@ extern "C" int rnn_problem_plan(const rnn_problem* problem, rnn_plan_info* info)
                           : (p->esize == 2 && p->def_acts) ? RNN_PRODUCTS_F16_MFMA : RNN_PRODUCTS_F32_MFMA;
   else
     info->step_products = RNN_PRODUCTS_F32_VALU;
+  info->xw_chunk_steps = int32_t(p->xw_tc);
+  info->xw_slots = p->xw_slots;
   return RNN_OK;
 }
 
@@ -497,6 +523,7 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
   a.P = P;
   a.lens = reinterpret_cast<const int32_t*>(lens);
   a.xw = static_cast<const float*>(xw_scratch);
+  a.xw_tc = int(p.xw_tc);
   a.hbuf = hbuf;
   a.rsplit = rsplit;
   a.hsplit = hsplit;
@@ -525,38 +552,51 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
     return hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
-  // 1. input projection
-  if (p.S > 0) {
-    ProjArgs pa{};
-    pa.X = X;
-    pa.W = W;
-    pa.xw = static_cast<float*>(xw_scratch);
-    pa.M = p.S * p.B;
-    pa.N = p.G * p.H;
-    pa.K = p.I;
-    pa.S = p.S;
-    pa.B = p.B;
-    pa.layout = p.desc.layout;
-    pa.D = p.D;
-    pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
-    pa.H = p.H;
-    pa.f32_split = p.f32_split_proj;
-    // X as the Y [S,2,B,I/2] of a bidirectional layout-0 layer: rows in two
-    // pieces, the second (B-1)*I/2 elements after the end of the first
-    const bool split_x = p.desc.x_bidirectional_y && p.desc.layout == 0 && p.B > 1;
-    pa.xkh = split_x ? p.I / 2 : p.I;
-    pa.xjump = split_x ? (p.B - 1) * (p.I / 2) : 0;
-    // the state setup rides in the same launch (extra workgroups)
-    if ((e = launch_projection(pa, sa, p.desc.dtype, s)) != hipSuccess)
-      return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));
-  }
+  // 1. input projection: chunk c covers steps [c*tc, (c+1)*tc) and fills
+  // slot c & 1 of the projection scratch (one chunk unless the per-step
+  // engine runs it in chunks, interleaved with the steps below)
+  const int64_t tc = p.xw_tc;
+  const int64_t nchunks = p.steps > 0 ? (p.steps + tc - 1) / tc : 0;
+  ProjArgs pa{};
+  pa.X = X;
+  pa.W = W;
+  pa.N = p.G * p.H;
+  pa.K = p.I;
+  pa.S = p.S;
+  pa.B = p.B;
+  pa.layout = p.desc.layout;
+  pa.D = p.D;
+  pa.skip_block = (lstm && p.desc.input_forget) ? 2 : -1;
+  pa.H = p.H;
+  pa.f32_split = p.f32_split_proj;
+  pa.lens = reinterpret_cast<const int32_t*>(lens);
+  pa.rev[0] = a.dir_reverse[0];
+  pa.rev[1] = a.dir_reverse[1];
+  pa.steps = p.steps;
+  pa.out_dstride = tc * p.B * pa.N;
+  // X as the Y [S,2,B,I/2] of a bidirectional layout-0 layer: rows in two
+  // pieces, the second (B-1)*I/2 elements after the end of the first
+  const bool split_x = p.desc.x_bidirectional_y && p.desc.layout == 0 && p.B > 1;
+  pa.xkh = split_x ? p.I / 2 : p.I;
+  pa.xjump = split_x ? (p.B - 1) * (p.I / 2) : 0;
+  auto project = [&](int64_t c) -> hipError_t {
+    ProjArgs q = pa;
+    q.s0 = c * tc;
+    q.M = std::min<int64_t>(tc, p.steps - q.s0) * p.B;
+    q.xw = static_cast<float*>(xw_scratch) + (c & 1) * int64_t(p.D) * pa.out_dstride;
+    // the state setup rides in the first chunk's launch (extra workgroups)
+    SetupArgs none{};
+    return launch_projection(q, c == 0 ? sa : none, p.desc.dtype, s);
+  };
+  if (nchunks > 0 && (e = project(0)) != hipSuccess)
+    return fail(RNN_ERR_HIP, cell, "projection launch: %s", hipGetErrorString(e));
   if ((e = mark(1)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
   // 2. state setup (its own launch only when there is no projection)
-  if (p.S == 0 && (e = launch_setup(sa, s)) != hipSuccess)
+  if (nchunks == 0 && (e = launch_setup(sa, s)) != hipSuccess)
     return fail(RNN_ERR_HIP, cell, "setup launch: %s", hipGetErrorString(e));
   if ((e = mark(2)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));
   // 3. recurrent steps
-  if (p.S > 0 && p.steps > 0) {
+  if (nchunks > 0) {
     if (pers) {
       PersistentIO io{ih, ic, const_cast<char*>(Y), const_cast<char*>(Yh), const_cast<char*>(Yc), status};
       if ((e = launch_step_persistent(a, p, io, s)) != hipSuccess)
@@ -576,9 +616,15 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
           return fail(RNN_ERR_HIP, cell, "persistent matrix-core step launch: %s", hipGetErrorString(e));
         done = e == hipSuccess;
       }
-      for (int step = 0; !done && step < int(p.steps); ++step)
+      for (int step = 0; !done && step < int(p.steps); ++step) {
+        // the next chunk's projection, into the slot the chunk before this
+        // one used (its steps are enqueued before it on the stream)
+        if (step % tc == 0 && step > 0 && (e = project(step / tc)) != hipSuccess)
+          return fail(RNN_ERR_HIP, cell, "projection launch (chunk %lld): %s", (long long)(step / tc),
+                      hipGetErrorString(e));
         if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
           return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));
+      }
     }
   }
   if ((e = mark(3)) != hipSuccess) return fail(RNN_ERR_HIP, cell, "event record: %s", hipGetErrorString(e));

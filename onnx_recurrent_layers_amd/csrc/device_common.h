@@ -123,6 +123,29 @@ __device__ __forceinline__ int64_t x_row_off(const ProjArgs& a, int64_t m) {
 }
 __device__ __forceinline__ int64_t x_col(const ProjArgs& a, int64_t k) { return k + (k >= a.xkh ? a.xjump : 0); }
 
+// Element offset in X of the row that output row m (step s0 + m / B, batch
+// row m % B) of direction d of a projection launch reads: time s forward,
+// len_b - 1 - s backward while the row runs, time s after it has ended (never
+// read).
+__device__ __forceinline__ int64_t x_row_step(const ProjArgs& a, int d, int64_t m) {
+  const int64_t sl = m / a.B, b = m - sl * a.B;
+  const int64_t s = a.s0 + sl;
+  int64_t t = s;
+  if (a.rev[d]) {
+    int64_t L = a.lens ? a.lens[b] : a.S;
+    L = L < 0 ? 0 : (L > a.S ? a.S : L);
+    L = L < a.steps ? L : a.steps;
+    if (s < L) t = L - 1 - s;
+  }
+  return x_row_off(a, t * a.B + b);
+}
+
+// The [B][G*H] slab of the projection that step s of direction d reads.
+__device__ __forceinline__ const float* xw_slab(const StepArgs& a, int d, int s) {
+  const int q = s / a.xw_tc;
+  return a.xw + ((int64_t(q & 1) * a.D + d) * a.xw_tc + (s - q * a.xw_tc)) * int64_t(a.B) * (a.G * a.H);
+}
+
 // Index of a state tensor (initial_h, initial_c, Y_h, Y_c) for direction d,
 // batch row b, unit j: layout 0 [D][B][H], layout 1 [B][D][H].
 __device__ __forceinline__ int64_t state_index(int layout, int D, int B, int H, int d, int b, int j) {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void projection_kernel(ProjArgs a, SetupArgs s
   for (int i = 0; i < APER; ++i) {
     const int q = tid + i * 256, r = q / SEGROW;
     ak[i] = (q % SEGROW) * SEG;
-    ap[i] = (m0 + r < a.M) ? X + x_row_off(a, m0 + r) : nullptr;
+    ap[i] = (m0 + r < a.M) ? X + x_row_step(a, d, m0 + r) : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < BPER; ++i) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void projection_kernel(ProjArgs a, SetupArgs s
   }
 
   // 32x32 accumulator layout: element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
-  float* out = a.xw + int64_t(d) * a.M * a.N;
+  float* out = a.xw + int64_t(d) * a.out_dstride;
 #pragma unroll
   for (int i = 0; i < IM; ++i)
 #pragma unroll
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void projection_bf16x3_kernel(ProjArgs a, Setu
   for (int i = 0; i < APER; ++i) {
     const int q = tid + i * 256, r = q / SEGROW;
     ak[i] = (q % SEGROW) * SEG;
-    ap[i] = (m0 + r < a.M) ? X + x_row_off(a, m0 + r) : nullptr;
+    ap[i] = (m0 + r < a.M) ? X + x_row_step(a, d, m0 + r) : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < BPER; ++i) {
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void projection_bf16x3_kernel(ProjArgs a, Setu
     __syncthreads();
   }
 
-  float* out = a.xw + int64_t(d) * a.M * a.N;
+  float* out = a.xw + int64_t(d) * a.out_dstride;
 #pragma unroll
   for (int i = 0; i < IM; ++i)
 #pragma unroll
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void projection_small_kernel(ProjArgs a, Setup
   // in both operands, so that such a product is exactly zero; a row past M or
   // N feeds only outputs that are dropped.  The mask is a bit mask, not a
   // select, which keeps the compiler from moving the loads into branches.
-  const T* ap = X + x_row_off(a, m0 + r32 < a.M ? m0 + r32 : a.M - 1);
+  const T* ap = X + x_row_step(a, d, m0 + r32 < a.M ? m0 + r32 : a.M - 1);
   const T* bp = W + (n0 + r32 < a.N ? n0 + r32 : a.N - 1) * a.K;
   // (rows of X in two pieces: elements at or past kh lie `jump` further on;
   // W passes kh = K)
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256) void projection_small_kernel(ProjArgs a, Setup
   for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * half + (r & 3)][r32] = acc[r];
   __syncthreads();
   const int nw = int(nblk < 4 ? nblk : 4);  // waves that own a block
-  float* out = a.xw + int64_t(d) * a.M * a.N;
+  float* out = a.xw + int64_t(d) * a.out_dstride;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid + 256 * q, row = e >> 5, col = e & 31;

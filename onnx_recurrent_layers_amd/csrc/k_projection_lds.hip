@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
     const int row = (wave * kLoads + i) * 16 + (lane >> 2);
     seg[i] = (lane & 3) ^ ((row >> 2) & 3);
     const int64_t m = m0 + row, n = n0 + row;
-    xrow[i] = m < a.M ? unsigned(x_row_off(a, m) * ES) : kOOB;
+    xrow[i] = m < a.M ? unsigned(x_row_step(a, d, m) * ES) : kOOB;
     wrow[i] = n < a.N ? unsigned(n * K * ES) : kOOB;
   }
   auto fetch = [&](int kc, unsigned char* sa_, unsigned char* sb_) {
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
   chunk_barrier<0>();   // the loads past the end have landed before the workgroup ends
 
   // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
-  float* out = a.xw + int64_t(d) * a.M * a.N;
+  float* out = a.xw + int64_t(d) * a.out_dstride;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll

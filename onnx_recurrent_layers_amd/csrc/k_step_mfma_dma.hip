@@ -130,7 +130,7 @@ struct EpiIn {
 // scratch memory.
 struct EpiCtx {
   __amdgpu_buffer_rsrc_t bias, peep;   // absent vector: size 0, loads return zeros without traffic
-  const float* xw;      // this direction's Xw, [S][B][G*H]
+  const float* xw;      // the projection slab of this step and direction, [B][G*H]
   const float* hprev;   // h of this step, [B][H]
   float* hnext;         // h of the next step, [B][H]
   void* Y;              // outputs (or null), written as the step finishes each element
@@ -183,7 +183,7 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d, int 
     c.act[k].beta = uniform(a.act[i].beta);
   }
   const int64_t DBH = int64_t(a.D) * a.B * a.H, dBH = int64_t(d) * a.B * a.H;
-  c.xw = a.xw + int64_t(d) * a.S * a.B * c.GH;
+  c.xw = xw_slab(a, d, step);
   c.hprev = a.hbuf + int64_t(step & 1) * DBH + dBH;
   c.hnext = a.hbuf + int64_t((step + 1) & 1) * DBH + dBH;
   c.Y = a.Y;
@@ -291,8 +291,7 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
     for (int k = 0; k < 3; ++k) o.pp[k] = res_load<RT>(c.peep, k * H + j);
   }
   if (!o.live) return;
-  const int t = c.rev ? (L - 1 - s) : s;
-  const float* xw = c.xw + (int64_t(t) * c.B + b) * c.GH;
+  const float* xw = c.xw + int64_t(b) * c.GH;
   const int64_t si = int64_t(b) * H + j;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
@@ -414,8 +413,7 @@ __device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s
     const int r = e >> ujs, b = b0 + r;
     const int L = len_s[r];
     const bool live = b < c.B && j < c.H && c.s < L;
-    const int t = live ? (c.rev ? L - 1 - c.s : c.s) : 0;
-    const int64_t row = live ? (int64_t(t) * c.B + b) * c.GH + j : 0;
+    const int64_t row = live ? int64_t(b) * c.GH + j : 0;
     const int64_t si = live ? int64_t(b) * c.H + j : 0;
     float* dst = planes + k * kMThreads + wave * 64;
 #pragma unroll

@@ -46,6 +46,11 @@ struct Problem {
   int64_t steps = 0;  // steps run: max_length or S
   int esize = 4;      // element size of float tensors
   size_t xw_bytes = 0;
+  // the projection scratch: xw_slots (1 or 2) slots of xw_tc steps each; two
+  // slots form a ring through which the projection runs chunk by chunk,
+  // ahead of the steps
+  int64_t xw_tc = 0;
+  int xw_slots = 1;
   StateLayout st{};
   int engine = RNN_ENGINE_LAUNCH;
   bool def_acts = false;  // every activation slot holds the cell's ONNX default
@@ -79,7 +84,13 @@ struct StepArgs {
   const void* bias;        // [D][2*G*H] or null
   const void* P;           // [D][3*H] or null
   const int32_t* lens;     // [B] or null
-  const float* xw;         // [D][S][B][G*H]
+  // the projection, step-major: slab (d, s) [B][G*H] holds, in row b, the
+  // projection of the X row that step s of batch row b of direction d reads
+  // (time s, or len_b - 1 - s for a reverse direction).  Chunked: a ring of
+  // two slots of xw_tc steps each, [slot][D][xw_tc][B][G*H], step s in slot
+  // (s / xw_tc) & 1; unchunked: xw_tc = S, one slot.
+  const float* xw;
+  int xw_tc;
   float* hbuf;             // [2][D][B][H]: slot s & 1 holds h of step s
   void* Y;                 // [S][D][B][H] (layout 0) or [B][S][D][H] (layout 1), or null
   void* Y_h;               // [D][B][H] (layout 0) or [B][D][H] (layout 1), or null
@@ -107,7 +118,14 @@ struct StepArgs {
 struct ProjArgs {
   const void* X;      // layout-mapped rows
   const void* W;      // [D][N][K]
-  float* xw;          // [D][M][N], M = S*B (row t*B+b)
+  float* xw;          // output row m of direction d at xw + d * out_dstride + m * N
+  int64_t out_dstride;
+  // output row m = (s - s0) * B + b is the projection of the X row that step
+  // s of batch row b reads: time s forward, len_b - 1 - s in a reverse
+  // direction (rev[d]); rows of a step past the row's length take time s
+  const int32_t* lens;
+  int rev[2];
+  int64_t s0, steps;
   int64_t M, N, K;
   int64_t S, B;
   int layout;

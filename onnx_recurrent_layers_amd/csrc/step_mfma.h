@@ -56,7 +56,7 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float
     const int L = len_s[r];
     if (s >= L) continue;
     const int t = a.dir_reverse[d] ? (L - 1 - s) : s;
-    const float* xw = a.xw + ((int64_t(d) * S + t) * B + b) * GH;
+    const float* xw = xw_slab(a, d, m.step) + int64_t(b) * GH;
     const int64_t sidx = int64_t(b) * H + j;
     const float* rrow = rec + r * LDR;
     auto pre = [&](int gi, int g) {

@@ -1,9 +1,8 @@
 // step_wave.h -- one wave's share of a recurrent step: the recurrent product
 // rec = R[d] . h_prev of one hidden unit for up to kRows batch rows, fused with
 // the gate arithmetic of cells.h ("Recurrent layers" page, "How a layer runs",
-// item 3).  Used by the per-step kernel (one wave per unit and row block) and
-// by the persistent engine's fallback (the waves of one workgroup walking every
-// unit of a direction).  Internal.
+// item 3).  Used by the per-step kernel (one wave per unit and row block).
+// Internal.
 #pragma once
 
 #include "cells.h"
@@ -94,7 +93,7 @@ __device__ __forceinline__ void step_wave(const StepArgs& a, int s, int phase, i
   const int b = b0 + lane;
   const int t = a.dir_reverse[d] ? (Lr - 1 - s) : s;
   const int GH = G * H;
-  const float* xw = a.xw + ((int64_t(d) * a.S + t) * B + b) * GH;
+  const float* xw = xw_slab(a, d, s) + int64_t(b) * GH;
   const T* bias = a.bias ? static_cast<const T*>(a.bias) + int64_t(d) * 2 * GH : nullptr;
   const Act* acts = a.act + d * a.slots;
   const int64_t sidx = int64_t(b) * H + j;  // within direction d

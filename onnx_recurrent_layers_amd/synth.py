@@ -53,6 +53,8 @@ class LayerSpec:
     # X is the Y of a bidirectional layer of the same layout, read in place
     # (layout 0: [S, 2, B, input/2] read as [S, B, input])
     x_bidirectional_y: int = 0
+    # the projection in chunks of this many steps (0: the library chooses)
+    xw_chunk_steps: int = 0
 
     @property
     def num_directions(self) -> int:

@@ -250,8 +250,37 @@ def test_sizes_at_the_limits(lib, cell, kw):
     h = rl.rnn_problem_create(rl.make_desc(spec(cell, **kw), "launch"))
     xw, _ = rl.rnn_scratch_size(h)
     G = {"LSTM": 4, "GRU": 3, "RNN": 1}[cell]
-    assert xw == 4 * kw["seq"] * kw["batch"] * G * kw["hidden"]
+    per_step = 4 * kw["batch"] * G * kw["hidden"]
+    full = kw["seq"] * per_step
+    # beyond 512 MiB the per-step engine runs the projection in chunks, a
+    # ring of two slots of 256 MiB
+    tc = kw["seq"] if full <= 512 << 20 else min(kw["seq"], max(1, (256 << 20) // per_step))
+    slots = 2 if tc < kw["seq"] else 1
+    assert xw == slots * tc * per_step
+    info = rl.rnn_problem_plan(h)
+    assert (info.xw_slots, info.xw_chunk_steps) == (slots, tc)
     rl.rnn_problem_destroy(h)
+
+
+@pytest.mark.parametrize("engine,chunk,want_tc,slots", [("launch", 3, 3, 2), ("launch", 0, 10, 1), ("launch", 10, 10, 1),
+                                                        ("launch", 25, 10, 1), ("persistent", 3, 10, 1)])
+def test_projection_chunks(lib, engine, chunk, want_tc, slots):
+    """The projection in chunks of the requested steps, a ring of two slots,
+    on the per-step engine; the persistent engines take one chunk."""
+    s = spec("GRU", seq=10, batch=3, hidden=8, input=5, direction="bidirectional", xw_chunk_steps=chunk)
+    h = rl.rnn_problem_create(rl.make_desc(s, engine))
+    info = rl.rnn_problem_plan(h)
+    assert (info.xw_chunk_steps, info.xw_slots) == (want_tc, slots)
+    xw, _ = rl.rnn_scratch_size(h)
+    assert xw == slots * want_tc * 4 * 2 * 3 * 3 * 8
+    nchunks = -(-10 // want_tc)
+    if engine == "launch":   # projection chunks + two launches per step (linear_before_reset = 0)
+        assert info.launches == nchunks + 2 * 10
+    rl.rnn_problem_destroy(h)
+    d = rl.make_desc(s, engine)
+    d.xw_chunk_steps = -1
+    rc, msg, _ = create_err(d)
+    assert rc == rl.RNN_ERR_SHAPE and "xw_chunk_steps" in msg
 
 
 @pytest.mark.parametrize("kw", [dict(batch=9, hidden=41), dict(batch=15, hidden=39), dict(batch=3, hidden=5000),

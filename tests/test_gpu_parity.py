@@ -37,6 +37,16 @@ def check(spec, inputs, engine="auto", offsets=None, twice=True, what=""):
 # ---------------------------------------------------------------------------
 # projection (stage 1) against the oracle's plain product, read from scratch
 # ---------------------------------------------------------------------------
+def step_rows(X, layout, S, B, d):
+    """A operand of direction d in the projection scratch's step order (full
+    lengths): row s*B + b is X at time s (forward, d = 0) or S-1-s (the
+    reverse direction, d = 1)."""
+    Xs = X if layout == 0 else X.transpose(1, 0, 2)
+    if d == 1:
+        Xs = Xs[::-1]
+    return np.ascontiguousarray(Xs).reshape(S * B, -1)
+
+
 @pytest.mark.parametrize("dtype,layout", [("f32", 0), ("f16", 0), ("f32", 1), ("f16", 1)])
 def test_projection_scratch(dtype, layout):
     import torch
@@ -48,9 +58,8 @@ def test_projection_scratch(dtype, layout):
     torch.cuda.synchronize()
     D, S, B, G, H, I = 2, spec.seq, spec.batch, 4, spec.hidden, spec.input
     xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
-    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
-    A = X.reshape(S * B, I)
     for d in range(D):
+        A = step_rows(inp["X"], layout, S, B, d)
         ref = oracle.projection(A, inp["W"][d])
         err = np.max(np.abs(xw[d].astype(np.float64) - ref))
         assert err <= 1e-4, (d, err)
@@ -81,9 +90,8 @@ def test_projection_small_kernel(dtype, layout, cell, input_forget, S, B, I, H, 
     torch.cuda.synchronize()
     D, G = 2, spec.gates
     xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
-    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
-    A = X.reshape(S * B, I)
     for d in range(D):
+        A = step_rows(inp["X"], layout, S, B, d)
         ref = oracle.projection(A, inp["W"][d])
         cols = np.ones(G * H, bool)
         if input_forget:
@@ -115,9 +123,8 @@ def test_projection_scratch_bf16x3(layout, S, B, I, H, monkeypatch):
     torch.cuda.synchronize()
     D, G = 2, 3
     xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
-    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
-    A = X.reshape(S * B, I)
     for d in range(D):
+        A = step_rows(inp["X"], layout, S, B, d)
         ref = oracle.projection(A, inp["W"][d])
         bound = 2.0 ** -15 * (np.abs(A.astype(np.float64)) @ np.abs(inp["W"][d].astype(np.float64)).T) + 1e-30
         err = np.abs(xw[d].astype(np.float64) - ref)
@@ -142,9 +149,8 @@ def test_projection_lds_bf16x3(layout, cell, input_forget, S, B, I, H, monkeypat
     torch.cuda.synchronize()
     D, G = 2, spec.gates
     xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
-    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
-    A = X.reshape(S * B, I)
     for d in range(D):
+        A = step_rows(inp["X"], layout, S, B, d)
         ref = oracle.projection(A, inp["W"][d])
         bound = 2.0 ** -15 * (np.abs(A.astype(np.float64)) @ np.abs(inp["W"][d].astype(np.float64)).T) + 1e-30
         cols = np.ones(G * H, bool)
@@ -187,15 +193,75 @@ def test_projection_lds_tiles(layout, cell, input_forget, S, B, I, H, monkeypatc
     torch.cuda.synchronize()
     D, G = 2, spec.gates
     xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(D, S * B, G * H).cpu().numpy()
-    X = inp["X"] if layout == 0 else inp["X"].transpose(1, 0, 2)
-    A = X.reshape(S * B, I)
     for d in range(D):
+        A = step_rows(inp["X"], layout, S, B, d)
         ref = oracle.projection(A, inp["W"][d])
         cols = np.ones(G * H, bool)
         if input_forget:
             cols[2 * H:3 * H] = False     # the f block is not computed
         err = np.max(np.abs(xw[d][:, cols].astype(np.float64) - ref[:, cols]))
         assert err <= 1e-3, (d, err)
+
+
+def test_projection_scratch_step_order_with_lengths():
+    """The reverse direction with sequence lengths: row b of step s holds the
+    projection of X at time len_b - 1 - s while the row runs."""
+    import torch
+    S, B, I, H = 9, 6, 24, 20
+    spec = LayerSpec("RNN", seq=S, batch=B, input=I, hidden=H, direction="bidirectional", dtype="f32", lens=True,
+                     outputs=("Y_h",))
+    inp = make_inputs(spec, 15)
+    inp["sequence_lens"] = np.array([9, 0, 4, 1, 7, 12], np.int32)
+    _, layer = gpu_layer(spec, inp, engine="launch", return_layer=True)
+    torch.cuda.synchronize()
+    xw = layer.xw[: layer.xw_bytes].view(torch.float32).view(2, S, B, H).cpu().numpy()
+    for d in range(2):
+        ref = oracle.projection(inp["X"].reshape(S * B, I), inp["W"][d]).reshape(S, B, H)
+        for b, Lb in enumerate(np.clip(inp["sequence_lens"], 0, S)):
+            for st in range(Lb):
+                t = st if d == 0 else Lb - 1 - st
+                assert np.max(np.abs(xw[d, st, b] - ref[t, b])) <= 1e-4, (d, st, b)
+
+
+# The projection in chunks through a ring of two slots (xw_chunk_steps), on
+# the per-step engines: chunks of 3 over 10 steps (the ring wraps three times
+# and the last chunk is short), the vector kernel and the matrix-core step,
+# reverse rows with their own lengths, both layouts, a row split in two
+# pieces (x_bidirectional_y); against the oracle, twice bit-identical.
+CHUNKS = [("LSTM", 5, "f32", 0, 3), ("GRU", 18, "f16", 1, 3), ("RNN", 20, "f32", 0, 4), ("LSTM", 17, "f16", 0, 1),
+          ("GRU", 3, "f32", 1, 7)]
+
+
+@pytest.mark.parametrize("cell,B,dtype,layout,chunk", CHUNKS, ids=[f"{c}-B{b}-{d}-L{l}-c{k}" for c, b, d, l, k in CHUNKS])
+def test_projection_in_chunks(cell, B, dtype, layout, chunk):
+    import onnx_recurrent_layers_amd as rl
+    spec = LayerSpec(cell, seq=10, batch=B, input=26, hidden=40, direction="bidirectional", layout=layout,
+                     dtype=dtype, init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM",
+                     clip=3.0, xw_chunk_steps=chunk, outputs=("Y", "Y_h", "Y_c"))
+    layer = rl.Layer(spec, engine="launch", device="cuda:0")
+    assert layer.plan.xw_slots == 2 and layer.plan.xw_chunk_steps == chunk
+    inp = make_inputs(spec, 121, Dists(sequence_lens=("I", 0, 10), W=("U", -0.3, 0.3), R=("U", -0.3, 0.3)))
+    check(spec, inp, engine="launch", what=f"chunks of {chunk} {cell} B{B} {dtype} L{layout}")
+
+
+def test_projection_in_chunks_split_rows():
+    """A stacked layout-0 layer (rows in two pieces) with its projection in
+    chunks."""
+    import onnx_recurrent_layers_amd as rl
+    S, B, H1 = 10, 18, 16
+    s1 = LayerSpec("GRU", seq=S, batch=B, input=12, hidden=H1, direction="bidirectional", layout=0, dtype="f32",
+                   lens=True, outputs=("Y",))
+    in1 = make_inputs(s1, 123, Dists(sequence_lens=("I", 1, S)))
+    y1 = rl.run(s1, in1, outputs=("Y",))["Y"]
+    s2 = LayerSpec("LSTM", seq=S, batch=B, input=2 * H1, hidden=24, direction="bidirectional", layout=0, dtype="f32",
+                   lens=True, xw_chunk_steps=4, outputs=("Y", "Y_h"))
+    in2 = make_inputs(s2, 124)
+    in2["sequence_lens"] = in1["sequence_lens"]
+    dev = rl.to_device({k: v for k, v in in2.items() if k != "X"})
+    got = rl.run(s2.replace(x_bidirectional_y=1), {**dev, "X": y1}, engine="launch", outputs=s2.outputs)
+    xt = y1.permute(0, 2, 1, 3).contiguous().view(S, B, 2 * H1).cpu().numpy()
+    ref = oracle.run(s2, {**in2, "X": xt}, outputs=s2.outputs)
+    compare(s2, {k: v.cpu().numpy() for k, v in got.items()}, ref, what="chunked split rows")
 
 
 # ---------------------------------------------------------------------------
