@@ -260,7 +260,7 @@ def cpu_baseline(name, spec, inputs, cpu_seconds: float, single_thread: bool = F
 
 
 def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_seconds: float,
-            single_thread: bool = False) -> dict:
+            single_thread: bool = False, xw_chunk_steps: int = 0) -> dict:
     """One workload: latency, throughput, stage times, the step kernel against
     the bounds that apply to it, the projection against the peak of the units
     it runs on, and the oracle baseline."""
@@ -269,6 +269,8 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
     from onnx_recurrent_layers_amd import synth
 
     spec, inputs = synth.config(name)
+    if xw_chunk_steps:
+        spec = spec.replace(xw_chunk_steps=xw_chunk_steps)
     dev = torch.device("cuda", 0)
     dt = torch.float32 if spec.dtype == "f32" else torch.float16
     tens = rl.to_device(inputs, "cuda:0")
@@ -312,6 +314,7 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
         "stage_ms_median": {k: round(v, 5) for k, v in st.items()},
         "per_step_us": round(per_step_us, 3), "step_launches": plan.step_launches, "step_launch_us": round(launch_ms * 1e3, 3),
         "step_products": step_kind, "step_bounds": bounds, "fallback_workgroups": run.fallback_workgroups,
+        "xw_chunk_steps": plan.xw_chunk_steps, "xw_slots": plan.xw_slots, "xw_scratch_bytes": layer.xw_bytes,
     }
     if floors and engine_name == "persistent" and plan.step_products in (0, 2) and spec.batch <= 8:
         fl = step_floors(spec, dt)
@@ -357,6 +360,8 @@ def main() -> int:
     ap.add_argument("--extra", default=",".join(EXTRA_CONFIGS),
                     help="other workloads measured after the main one and reported under 'configs' "
                          "(comma-separated; empty for none)")
+    ap.add_argument("--xw-chunk-steps", type=int, default=0,
+                    help="the main workload's projection in chunks of this many steps (0: the library chooses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the step-floor layers (for profiler runs, whose kernel statistics then cover the "
@@ -386,7 +391,8 @@ def main() -> int:
 
     cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
     m = measure(args.config, args.engine, args.steps, args.warmup, not args.no_floors, cpu_s,
-                single_thread=args.config in ("C1", "C2") and not args.no_cpu_baseline)
+                single_thread=args.config in ("C1", "C2") and not args.no_cpu_baseline,
+                xw_chunk_steps=args.xw_chunk_steps)
     spec = m.pop("_spec")
     hb = m["step_bounds"]["hbm"]
     line = {

@@ -46,6 +46,10 @@
  *       RNN_SMALL_PROJECTION=0|1    small-layer projection off or on
  *       RNN_PROJ_LDS_MIN_TILES=n    tile count from which the 256x256
  *                                   projection is taken
+ *       RNN_CHUNK_OVERLAP=1         a chunked projection runs on a second
+ *                                   stream (default priority), each chunk
+ *                                   overlapping the steps of the chunk before
+ *                                   (off by default: measured no faster)
  */
 #ifndef ONNX_RNN_MI355X_H
 #define ONNX_RNN_MI355X_H
@@ -122,8 +126,8 @@ typedef struct {
                                   nothing. */
   int64_t xw_chunk_steps;      /* the input projection in chunks of this many steps, through a ring of two
                                   chunks in the projection scratch (the page's "Scratch": XwLength grows with
-                                  the layer), each chunk's projection enqueued ahead of its steps and
-                                  overlapping the steps of the chunk before: 0 lets the library choose (one
+                                  the layer), each chunk's projection enqueued right before its steps (or
+                                  ahead of them on a second stream, RNN_CHUNK_OVERLAP): 0 lets the library choose (one
                                   chunk, unless the whole projection exceeds 512 MiB); n > 0 asks for chunks
                                   of n steps.  Only the per-step engine (RNN_ENGINE_LAUNCH) runs in chunks;
                                   the persistent engines read every step's projection in their one launch

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -59,6 +60,39 @@ bool mul4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The stream on which the per-step engine runs the later chunks of a chunked
+// projection, beside the caller's stream: one per device, created on first
+// use (default priority), kept until the process ends.
+hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev] && (e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking)) != hipSuccess) return e;
+  *out = streams[dev];
+  return hipSuccess;
+}
+
+// Events ordering the two streams of one chunked rnn_encode (created and
+// destroyed per call: calls on different threads never share them).
+struct ChunkEvents {
+  hipEvent_t ev[5] = {};   // fork, projection done [2], steps done [2]
+  ~ChunkEvents() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  hipError_t create() {
+    for (hipEvent_t& e : ev) {
+      hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+};
 
 // Largest tensor byte count accepted: keeps every offset computation far from
 // 64-bit overflow.
@@ -408,7 +442,7 @@ int resolve(const rnn_tensor& t, int esize, int cell, const char* name, bool req
 namespace {
 
 int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
-                void* stream, void* const* events);
+                void* stream, void* const* events, bool may_fork);
 
 }  // namespace
 
@@ -416,7 +450,8 @@ namespace rnnhip {
 
 int encode_layer(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
                  void* stream) {
-  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr);
+  // (no second stream: this path serves callers that cannot create objects)
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr, false);
 }
 
 int set_error(int code, int cell, const char* msg) { return fail(code, cell, "%s", msg); }
@@ -425,19 +460,26 @@ int set_error(int code, int cell, const char* msg) { return fail(code, cell, "%s
 
 extern "C" int rnn_encode(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch,
                           void* state_scratch, void* stream) {
-  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr);
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, nullptr, true);
 }
 
 extern "C" int rnn_encode_timed(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch,
                                 void* state_scratch, void* stream, void* const events[5]) {
-  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, events);
+  return encode_impl(problem, ops, xw_scratch, state_scratch, stream, events, true);
 }
 
 namespace {
 
 int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_scratch, void* state_scratch,
-                void* stream, void* const* events) {
+                void* stream, void* const* events, bool may_fork) {
   g_error.clear();
+  // a chunked projection may run on a second stream, overlapping the steps
+  // of the chunk before (RNN_CHUNK_OVERLAP=1).  Off by default: measured on
+  // the RNN 1024/256/1024/2048 layer it gains nothing (40.2 ms against 40.0
+  // ms on the caller's stream), since every step kernel holds the LDS of
+  // every compute unit and the projection's tiles only run between steps.
+  bool chunk_overlap = false;
+  if (const char* env = std::getenv("RNN_CHUNK_OVERLAP")) chunk_overlap = may_fork && std::atoi(env) != 0;
   if (!problem) return fail(RNN_ERR_ARG, -1, "problem: NULL");
   const Problem& p = *reinterpret_cast<const Problem*>(problem);
   const int cell = p.desc.cell;
@@ -616,14 +658,54 @@ int encode_impl(const rnn_problem* problem, const rnn_operands* ops, void* xw_sc
           return fail(RNN_ERR_HIP, cell, "persistent matrix-core step launch: %s", hipGetErrorString(e));
         done = e == hipSuccess;
       }
-      for (int step = 0; !done && step < int(p.steps); ++step) {
-        // the next chunk's projection, into the slot the chunk before this
-        // one used (its steps are enqueued before it on the stream)
-        if (step % tc == 0 && step > 0 && (e = project(step / tc)) != hipSuccess)
-          return fail(RNN_ERR_HIP, cell, "projection launch (chunk %lld): %s", (long long)(step / tc),
-                      hipGetErrorString(e));
-        if ((e = mfma ? launch_step_mfma(a, p, step, s) : launch_step_generic(a, step, s)) != hipSuccess)
-          return fail(RNN_ERR_HIP, cell, "step %d launch: %s", step, hipGetErrorString(e));
+      // Chunks after the first: with overlap, each projection runs on the
+      // side stream one chunk ahead of the steps (chunk c+1's projection
+      // while chunk c steps), each chunk's steps wait for their projection,
+      // and a projection waits for the steps of the chunk that last used its
+      // slot; without, each projection is enqueued on the caller's stream
+      // right before its chunk's first step.
+      ChunkEvents ev;
+      hipStream_t side = nullptr;
+      const bool overlap = !done && nchunks > 1 && chunk_overlap;
+      if (overlap) {
+        if ((e = ev.create()) != hipSuccess || (e = side_stream(&side)) != hipSuccess)
+          return fail(RNN_ERR_HIP, cell, "chunk streams: %s", hipGetErrorString(e));
+        // the side stream starts after everything enqueued so far on the
+        // caller's stream (an earlier call may still read the ring)
+        if ((e = hipEventRecord(ev.ev[0], s)) != hipSuccess || (e = hipStreamWaitEvent(side, ev.ev[0], 0)) != hipSuccess)
+          return fail(RNN_ERR_HIP, cell, "chunk fork: %s", hipGetErrorString(e));
+      }
+      auto project_on = [&](int64_t c, hipStream_t st) -> hipError_t {
+        ProjArgs q = pa;
+        q.s0 = c * tc;
+        q.M = std::min<int64_t>(tc, p.steps - q.s0) * p.B;
+        q.xw = static_cast<float*>(xw_scratch) + (c & 1) * int64_t(p.D) * pa.out_dstride;
+        SetupArgs none{};
+        return launch_projection(q, none, p.desc.dtype, st);
+      };
+      if (overlap) {
+        if ((e = project_on(1, side)) != hipSuccess || (e = hipEventRecord(ev.ev[1 + 1], side)) != hipSuccess)
+          return fail(RNN_ERR_HIP, cell, "projection launch (chunk 1): %s", hipGetErrorString(e));
+      }
+      for (int64_t c = 0; !done && c < nchunks; ++c) {
+        if (c > 0) {
+          if (overlap) e = hipStreamWaitEvent(s, ev.ev[1 + (c & 1)], 0);
+          else e = project_on(c, s);
+          if (e != hipSuccess)
+            return fail(RNN_ERR_HIP, cell, "projection (chunk %lld): %s", (long long)c, hipGetErrorString(e));
+        }
+        const int64_t last = std::min<int64_t>((c + 1) * tc, p.steps);
+        for (int64_t step = c * tc; step < last; ++step)
+          if ((e = mfma ? launch_step_mfma(a, p, int(step), s) : launch_step_generic(a, int(step), s)) != hipSuccess)
+            return fail(RNN_ERR_HIP, cell, "step %lld launch: %s", (long long)step, hipGetErrorString(e));
+        if (overlap && c + 2 < nchunks) {
+          // chunk c+2 reuses chunk c's slot: after chunk c's steps
+          if ((e = hipEventRecord(ev.ev[3 + (c & 1)], s)) != hipSuccess ||
+              (e = hipStreamWaitEvent(side, ev.ev[3 + (c & 1)], 0)) != hipSuccess ||
+              (e = project_on(c + 2, side)) != hipSuccess || (e = hipEventRecord(ev.ev[1 + (c & 1)], side)) != hipSuccess)
+            return fail(RNN_ERR_HIP, cell, "projection launch (chunk %lld): %s", (long long)(c + 2),
+                        hipGetErrorString(e));
+        }
       }
     }
   }

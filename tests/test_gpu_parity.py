@@ -227,14 +227,18 @@ def test_projection_scratch_step_order_with_lengths():
 # the per-step engines: chunks of 3 over 10 steps (the ring wraps three times
 # and the last chunk is short), the vector kernel and the matrix-core step,
 # reverse rows with their own lengths, both layouts, a row split in two
-# pieces (x_bidirectional_y); against the oracle, twice bit-identical.
+# pieces (x_bidirectional_y); on the caller's stream and with each chunk's
+# projection on a second stream ahead of the steps (RNN_CHUNK_OVERLAP); against
+# the oracle, twice bit-identical.
 CHUNKS = [("LSTM", 5, "f32", 0, 3), ("GRU", 18, "f16", 1, 3), ("RNN", 20, "f32", 0, 4), ("LSTM", 17, "f16", 0, 1),
           ("GRU", 3, "f32", 1, 7)]
 
 
 @pytest.mark.parametrize("cell,B,dtype,layout,chunk", CHUNKS, ids=[f"{c}-B{b}-{d}-L{l}-c{k}" for c, b, d, l, k in CHUNKS])
-def test_projection_in_chunks(cell, B, dtype, layout, chunk):
+@pytest.mark.parametrize("overlap", ["0", "1"])
+def test_projection_in_chunks(cell, B, dtype, layout, chunk, overlap, monkeypatch):
     import onnx_recurrent_layers_amd as rl
+    monkeypatch.setenv("RNN_CHUNK_OVERLAP", overlap)
     spec = LayerSpec(cell, seq=10, batch=B, input=26, hidden=40, direction="bidirectional", layout=layout,
                      dtype=dtype, init_h=True, init_c=cell == "LSTM", lens=True, peephole=cell == "LSTM",
                      clip=3.0, xw_chunk_steps=chunk, outputs=("Y", "Y_h", "Y_c"))
