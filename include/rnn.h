@@ -61,6 +61,12 @@
 extern "C" {
 #endif
 
+/* Status of every call.  The page's exceptions map onto them: a shape
+ * exception naming the cell and the argument ("Scratch": checked in safe
+ * arithmetic before anything is recorded) is RNN_ERR_SHAPE or RNN_ERR_ARG,
+ * an option on the wrong cell ("Semantics": anything else throws) is
+ * RNN_ERR_ARG, and the unsupported-layer exception ("Scratch": larger layers
+ * throw) is RNN_ERR_UNSUPPORTED. */
 typedef enum {
   RNN_OK = 0,
   RNN_ERR_ARG = 1,         /* a NULL or malformed argument, an option on the wrong cell */
@@ -191,12 +197,20 @@ void rnn_problem_destroy(rnn_problem* problem);
  * be 256-byte aligned; they may be two regions of one arena. */
 int rnn_scratch_size(const rnn_problem* problem, size_t* xw_bytes, size_t* state_bytes);
 
-/* Enqueue one layer on `stream` (a hipStream_t; NULL is the default stream).
+/* Enqueue one layer on `stream` (a hipStream_t; NULL is the default stream):
+ * the four stages of "How a layer runs" on the "Recurrent layers" page (the
+ * page's Encode into a caller's command encoder), with the edge rules of its
+ * "Semantics" list and the arithmetic order of "Arithmetic and determinism".
  * Stages: the input projection (carrying the state setup), then the
  * recurrent steps, which write whichever of Y, Y_h, Y_c is requested as they
  * go (the setup writes the outputs no step reaches).  Batch = 0 enqueues
  * nothing; Seq = 0 writes only Y_h / Y_c (initial states or zeros).  All
- * checks run before the first launch; when one fails nothing is enqueued.
+ * checks run before the first launch ("Scratch": sizes, offsets and shapes
+ * are checked before anything is recorded); when one fails nothing is
+ * enqueued.  Arguments: `operands` as described above (device pointers with
+ * element offsets, owned by the caller); `xw_scratch` and `state_scratch` the
+ * caller's device buffers of at least the sizes rnn_scratch_size reports,
+ * 256-byte aligned (the page's xwScratch and stateScratch).
  * RNN_ERR_HIP (the runtime refused a launch) may come after earlier stages
  * were enqueued: the outputs are then undefined, and the scratch is in use
  * until the stream has finished that work.  sequence_lens is read on the
@@ -288,7 +302,10 @@ typedef struct {
 } rnn_run_status;
 int rnn_read_run_status(const rnn_problem* problem, const void* state_scratch, void* stream, rnn_run_status* out);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none): the cell
+ * (LSTM, GRU or RNN) and the argument at fault, as the page's shape
+ * exception names them ("Scratch").  The string is owned by the library and
+ * valid until the thread's next call. */
 const char* rnn_last_error(void);
 
 #ifdef __cplusplus
