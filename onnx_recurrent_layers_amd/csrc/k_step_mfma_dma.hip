@@ -29,11 +29,13 @@
 // fixed vector-memory count.
 //
 // LDS layout of a chunk: rows of 16-byte segments, unpadded; the segment of
-// logical index s of row r is stored at slot s ^ (r & 15), so that the 16
-// rows a matrix-core operand read touches land in 16 different bank groups.
-// The k index is permuted inside a chunk (lane group q of an operand takes a
-// contiguous quarter of the chunk), identically for h and R, so each lane
-// reads whole 16-byte segments; a sum over a permuted k range is the same sum.
+// logical index s of row r is stored at slot s ^ w(r & 15), w(r) = r for
+// rows of 16 segments and r with bit 0 copied to bit 4 for the 32-segment h
+// rows of the f16 mode, so that the 32 lanes of a half-wave operand read land
+// in 32 different 16-byte bank groups.  The k index is permuted inside a
+// chunk (step kk of lane group q takes segment 4kk + q), identically for h
+// and R, so each lane reads whole 16-byte segments; a sum over a permuted k
+// range is the same sum.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
@@ -67,6 +69,12 @@ __device__ __forceinline__ void chunk_barrier() {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Slot of segment s of LDS row r is s ^ row_swizzle(r & 15) (see above).
+template <int MODE>
+__device__ __forceinline__ int row_swizzle(int r) {
+  return MODE == 1 ? r | ((r & 1) << 4) : r;
 }
 
 template <int MODE> struct DmaGeo;
@@ -539,7 +547,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
   for (int i = 0; i < LA; ++i) {
     const int p = (wave * LA + i) * 64 + lane;
     const int r = p / ASEGS;
-    aseg[i] = (p % ASEGS) ^ (r & 15);
+    aseg[i] = (p % ASEGS) ^ row_swizzle<MODE>(r & 15);
     arow[i] = b0 + r < B ? unsigned(b0 + r) * unsigned(H) * AES : kOutOfRange;
   }
   // R segments: wave w owns column blocks w and w + 4 (CB of them); load i of
@@ -675,13 +683,13 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           bq[cb][j] = *reinterpret_cast<const f32x4*>(
-              Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * q + j) ^ r16) << 4));
+              Bs + ((wave + 4 * cb) * 16 + r16) * 256 + (((4 * j + q) ^ r16) << 4));
       f32x4 aq[NBI][4];
 #pragma unroll
       for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          aq[bi][j] = *reinterpret_cast<const f32x4*>(st + (bi * 16 + r16) * 256 + (((4 * q + j) ^ r16) << 4));
+          aq[bi][j] = *reinterpret_cast<const f32x4*>(st + (bi * 16 + r16) * 256 + (((4 * j + q) ^ r16) << 4));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -733,9 +741,9 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
         const int ci = RR && wave + 4 * cb >= ncb ? 0 : wave + 4 * cb;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          bv[cb][kk] = *reinterpret_cast<const hx8*>(Rb + (ci * 16 + r16) * 256 + (((4 * q + kk) ^ r16) << 4));
+          bv[cb][kk] = *reinterpret_cast<const hx8*>(Rb + (ci * 16 + r16) * 256 + (((4 * kk + q) ^ r16) << 4));
       }
-      // step kk takes the 8-element k group 4q + kk of both halves of h and
+      // step kk takes the 8-element k group 4kk + q of both halves of h and
       // of R (the same k for both operands)
       hx8 ah[NBI][4], al[NBI][4];
 #pragma unroll
@@ -743,8 +751,8 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const unsigned char* row = st + (bi * 16 + r16) * 512;
-          ah[bi][kk] = *reinterpret_cast<const hx8*>(row + (((4 * q + kk) ^ r16) << 4));
-          al[bi][kk] = *reinterpret_cast<const hx8*>(row + (((16 + 4 * q + kk) ^ r16) << 4));
+          ah[bi][kk] = *reinterpret_cast<const hx8*>(row + (((4 * kk + q) ^ row_swizzle<1>(r16)) << 4));
+          al[bi][kk] = *reinterpret_cast<const hx8*>(row + (((16 + 4 * kk + q) ^ row_swizzle<1>(r16)) << 4));
         }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)

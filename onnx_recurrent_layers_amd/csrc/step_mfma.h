@@ -37,7 +37,7 @@ template <typename T, int BM>
 __device__ __forceinline__ void mfma_epilogue(const MfmaStepArgs& m, const float* rec, const int* len_s, int b0,
                                               int j0, int d) {
   const StepArgs& a = m.a;
-  const int H = a.H, B = a.B, G = a.G, S = a.S;
+  const int H = a.H, B = a.B, G = a.G;
   const int s = m.step;
   const int tid = threadIdx.x;
   const int UJ = m.UJ;
