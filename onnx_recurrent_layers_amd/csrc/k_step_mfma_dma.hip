@@ -77,6 +77,20 @@ __device__ __forceinline__ int row_swizzle(int r) {
   return MODE == 1 ? r | ((r & 1) << 4) : r;
 }
 
+// Scheduling of one chunk's instructions: its D operand reads first, then
+// the L loads of a later chunk spread between its M matrix-core products (a
+// wave issues in order, so loads grouped ahead of the products hold the
+// products back while the memory unit accepts them).
+template <int D, int L, int M>
+__device__ __forceinline__ void interleave_chunk() {
+  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);   // LDS reads
+#pragma unroll
+  for (int g = 0; g < L; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // a memory load
+    __builtin_amdgcn_sched_group_barrier(0x008, (M + L - 1) / L, 0);   // matrix-core products
+  }
+}
+
 template <int MODE> struct DmaGeo;
 template <> struct DmaGeo<0> {           // f32 h, f32 R
   typedef float RT;
@@ -401,6 +415,8 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
 // Per-element planes of the elements after each thread's first: Xw of the Gp
 // computed blocks, then the state the cell reads (LSTM c, GRU h), then the
 // GRU z of the first pass.  Each plane holds n_el floats, element e at e.
+constexpr int kMaxEl = 64 * 64 / kMThreads;   // elements per thread of the largest tile (64 rows x 64 units)
+
 __host__ __device__ constexpr int epi_state_planes(int cell, int lbr, int phase) {
   return cell == RNN_CELL_LSTM ? 1 : cell == RNN_CELL_GRU ? 1 + (!lbr && phase == 1) : 0;
 }
@@ -413,13 +429,20 @@ __host__ __device__ constexpr int epi_state_planes(int cell, int lbr, int phase)
 __device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s, float* planes, int n_el, int ujs,
                                                int b0, int j0) {
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int E = n_el / kMThreads;
+  const int E = n_el / kMThreads;   // at most kMaxEl
   const int j = j0 + (tid & ((1 << ujs) - 1));   // the same unit for every element of this thread
   const int ns = epi_state_planes(c.cell, c.lbr, c.phase);
-  for (int k = 1; k < E; ++k) {
+  // the rows' lengths first, so that the loads below issue back to back
+  // instead of each behind an LDS read
+  int Ls[kMaxEl];
+#pragma unroll
+  for (int k = 1; k < kMaxEl; ++k) Ls[k] = k < E ? len_s[(tid + k * kMThreads) >> ujs] : 0;
+#pragma unroll
+  for (int k = 1; k < kMaxEl; ++k) {
+    if (k >= E) break;
     const int e = tid + k * kMThreads;
     const int r = e >> ujs, b = b0 + r;
-    const int L = len_s[r];
+    const int L = Ls[k];
     const bool live = b < c.B && j < c.H && c.s < L;
     const int64_t row = live ? int64_t(b) * c.GH + j : 0;
     const int64_t si = live ? int64_t(b) * c.H + j : 0;
@@ -699,6 +722,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
 #pragma unroll
             for (int bi = 0; bi < NBI; ++bi)
               acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[bi][j][e], bq[cb][j][e], acc[cb][bi], 0, 0, 0);
+      interleave_chunk<4 * CB + 4 * NBI, L, 16 * CB * NBI>();
     } else if constexpr (MODE == 2) {
       // step kk takes the 8-element k groups 4kk + q of both planes, the same
       // groups for h and R
@@ -730,6 +754,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
             acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bi][kk], bl[cb][kk], acc[cb][bi], 0, 0, 0);
             acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bi][kk], bh[cb][kk], acc[cb][bi], 0, 0, 0);
           }
+      interleave_chunk<4 * CB + 4 * NBI, L, 6 * CB * NBI>();
     } else {
       hx8 bv[CB][4];
       // resident R: this chunk's blocks (chunks past the end read the last
@@ -763,6 +788,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
             acc[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[bi][kk], bv[cb][kk], acc[cb][bi], 0, 0, 0);
             acc_lo[cb][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[bi][kk], bv[cb][kk], acc_lo[cb][bi], 0, 0, 0);
           }
+      interleave_chunk<4 * CB + 8 * NBI, L, 8 * CB * NBI>();
     }
     }
   }
