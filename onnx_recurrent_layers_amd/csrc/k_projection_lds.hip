@@ -64,6 +64,20 @@ __device__ __forceinline__ void chunk_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Scheduling of one chunk's instructions: its D operand reads first, then
+// the L loads of a later chunk spread between its M matrix-core products (a
+// wave issues in order: loads grouped ahead of the products would hold the
+// products back while the memory unit accepts them).
+template <int D, int L, int M>
+__device__ __forceinline__ void interleave_chunk() {
+  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);   // LDS reads
+#pragma unroll
+  for (int g = 0; g < L; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // a memory load
+    __builtin_amdgcn_sched_group_barrier(0x008, (M + L - 1) / L, 0);   // matrix-core products
+  }
+}
+
 // hi = bf16(x), lo = bf16(x - hi) of eight values
 __device__ __forceinline__ void split8(const f32x4 p, const f32x4 q, bx8& hi, bx8& lo) {
   const float x[8] = {p[0], p[1], p[2], p[3], q[0], q[1], q[2], q[3]};
@@ -124,12 +138,16 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
     xrow[i] = m < a.M ? unsigned(x_row_step(a, d, m) * ES) : kOOB;
     wrow[i] = n < a.N ? unsigned(n * K * ES) : kOOB;
   }
+  // X column of element k of a row (32-bit: every offset fits the resource)
+  const int xkh = int(a.xkh);
+  const unsigned xjump = unsigned(a.xjump);
   auto fetch = [&](int kc, unsigned char* sa_, unsigned char* sb_) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int k = kc * KC + seg[i] * SEGE;
+      const unsigned xc = unsigned(k) + (k >= xkh ? xjump : 0u);
       // a row outside the matrix starts at the out-of-range marker, so row + k stays out of range
-      const unsigned ox = k < K ? xrow[i] + unsigned(x_col(a, k)) * unsigned(ES) : kOOB;
+      const unsigned ox = k < K ? xrow[i] + xc * unsigned(ES) : kOOB;
       const unsigned ow = k < K ? wrow[i] + unsigned(k) * unsigned(ES) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, RNN_LDS_PTR(sa_ + (wave * kLoads + i) * 1024), 16, ox, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, RNN_LDS_PTR(sb_ + (wave * kLoads + i) * 1024), 16, ow, 0, 0, 0);
@@ -184,10 +202,11 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[j], al[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[j], ah[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[j], ah[i], acc[i][j], 0, 0, 0);
           }
+        interleave_chunk<16, 2 * kLoads, 48>();
         continue;
       }
 #pragma unroll
@@ -208,24 +227,41 @@ __global__ __launch_bounds__(256) void projection_lds_kernel(ProjArgs a, SetupAr
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);
       }
+      interleave_chunk<16, 2 * kLoads, 32>();
     }
   }
   chunk_barrier<0>();   // the loads past the end have landed before the workgroup ends
 
-  // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
+  // Each product block is taken transposed (W rows as the first operand), so
+  // that the 32x32 accumulator layout, element e of lane l at row
+  // 8*(e/4) + 4*(l/32) + e%4 and column l%32, puts four consecutive output
+  // columns n (block rows) of one output row m (block column) in elements
+  // 4t..4t+3 of a lane: one 16-byte store each when Xw rows are whole 16-byte
+  // groups.
   float* out = a.xw + int64_t(d) * a.out_dstride;
+  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 32 + r32;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        const int64_t n = n0 + wn * 128 + j * 32 + r32;
-        if (m < a.M && n < a.N) out[m * a.N + n] = acc[i][j][e];
+      for (int t = 0; t < 4; ++t) {
+        const int64_t n = n0 + wn * 128 + j * 32 + 8 * t + 4 * g;
+        if (m >= a.M) continue;
+        if (vec) {
+          if (n < a.N)
+            *reinterpret_cast<f32x4*>(out + m * a.N + n) =
+                f32x4{acc[i][j][4 * t], acc[i][j][4 * t + 1], acc[i][j][4 * t + 2], acc[i][j][4 * t + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.N) out[m * a.N + n + e] = acc[i][j][4 * t + e];
+        }
       }
+  }
 }
 
 // Takes the layer when the operands are rows of whole 16-byte segments (f16,

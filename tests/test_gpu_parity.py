@@ -179,6 +179,7 @@ def test_layers_with_bf16x3_projection(cell, monkeypatch):
     (1, "LSTM", 1, 9, 70, 136, 256),     # skipped f block of whole tiles, layout 1
     (1, "GRU", 0, 33, 17, 264, 96),
     (0, "RNN", 0, 40, 20, 520, 300),
+    (0, "GRU", 0, 11, 23, 64, 45),       # rows of Xw not in 16-byte groups (G*H odd): one value per store
 ])
 def test_projection_lds_tiles(layout, cell, input_forget, S, B, I, H, monkeypatch):
     """The 256x256 f16 projection loaded straight into LDS, forced onto small
