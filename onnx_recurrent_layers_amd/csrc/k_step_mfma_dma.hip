@@ -412,11 +412,11 @@ __device__ __forceinline__ void epi_finish(const EpiCtx& c, const EpiIn& o, cons
   }
 }
 
+constexpr int kMaxEl = 64 * 64 / kMThreads;   // elements per thread of the largest tile (64 rows x 64 units)
+
 // Per-element planes of the elements after each thread's first: Xw of the Gp
 // computed blocks, then the state the cell reads (LSTM c, GRU h), then the
 // GRU z of the first pass.  Each plane holds n_el floats, element e at e.
-constexpr int kMaxEl = 64 * 64 / kMThreads;   // elements per thread of the largest tile (64 rows x 64 units)
-
 __host__ __device__ constexpr int epi_state_planes(int cell, int lbr, int phase) {
   return cell == RNN_CELL_LSTM ? 1 : cell == RNN_CELL_GRU ? 1 + (!lbr && phase == 1) : 0;
 }
@@ -426,12 +426,53 @@ __host__ __device__ constexpr int epi_state_planes(int cell, int lbr, int phase)
 // bytes at its instruction's base + 4*l, which is element e's slot since the
 // wave's 64 elements are consecutive.  Elements that do not run load a valid
 // dummy address.
+// VEC (the per-step kernel) takes 16-byte loads where it can; the persistent
+// kernel keeps the one-value form (its code size and registers measured
+// better without the second form).
+template <bool VEC>
 __device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s, float* planes, int n_el, int ujs,
                                                int b0, int j0) {
   const int tid = threadIdx.x, wave = tid >> 6;
+  const int ns = epi_state_planes(c.cell, c.lbr, c.phase);
+  if (VEC && (c.H & 3) == 0 && uint64_t(c.B) * uint64_t(c.GH) * 4u < uint64_t(kOutOfRange)) {
+    // Four consecutive elements (one row, four units) per lane and 16 bytes
+    // per load: load w of the workgroup covers elements 256 (w + 1) ..
+    // 256 (w + 2) - 1, lane l of it elements + 4l .. + 4l + 3.  An element
+    // group that does not run (or reaches past H) reads as zeros.
+    const int lane = tid & 63;
+    const unsigned bh = unsigned(c.B) * unsigned(c.H) * 4u;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(c.xw), 0, int(unsigned(c.B) * unsigned(c.GH) * 4u), kRsrcWord3);
+    const float* st = c.cell == RNN_CELL_LSTM ? c.cst : c.hprev;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(st), 0, int(bh), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(c.zbuf, 0, int(bh), kRsrcWord3);
+    const int nw = n_el / kMThreads - 1;   // loads of the workgroup
+    for (int w = wave; w < nw; w += kMThreads / 64) {
+      const int e = (w + 1) * kMThreads + 4 * lane;
+      const int r = e >> ujs, b = b0 + r;
+      const int j = j0 + (e & ((1 << ujs) - 1));
+      const bool live = b < c.B && j + 3 < c.H && c.s < len_s[r];
+      float* dst = planes + (w + 1) * kMThreads;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        if (gi < c.Gp) {
+          const unsigned off = live ? (unsigned(b) * unsigned(c.GH) + unsigned(c.gate[gi] * c.H + j)) * 4u : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, RNN_LDS_PTR(dst + gi * n_el), 16, off, 0, 0, 0);
+        }
+      const unsigned so = live ? (unsigned(b) * unsigned(c.H) + unsigned(j)) * 4u : kOutOfRange;
+      if (ns > 0) {
+        if (c.coh) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RNN_LDS_PTR(dst + c.Gp * n_el), 16, so, 0, 0, 16);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RNN_LDS_PTR(dst + c.Gp * n_el), 16, so, 0, 0, 0);
+      }
+      if (ns > 1) {
+        if (c.coh) __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 16, so, 0, 0, 16);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, RNN_LDS_PTR(dst + (c.Gp + 1) * n_el), 16, so, 0, 0, 0);
+      }
+    }
+    return;
+  }
   const int E = n_el / kMThreads;   // at most kMaxEl
   const int j = j0 + (tid & ((1 << ujs) - 1));   // the same unit for every element of this thread
-  const int ns = epi_state_planes(c.cell, c.lbr, c.phase);
   // the rows' lengths first, so that the loads below issue back to back
   // instead of each behind an LDS read
   int Ls[kMaxEl];
@@ -819,7 +860,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
   // slot holds them), all loads in flight together
   constexpr bool DEF = MODE == 1;
   float* planes = reinterpret_cast<float*>(st1);
-  if (n_el > kMThreads) epi_tile_issue(ctx, len_s, planes, n_el, ujs, b0, j0);
+  if (n_el > kMThreads) epi_tile_issue<!PERS>(ctx, len_s, planes, n_el, ujs, b0, j0);
   epi_finish<RT, DEF>(ctx, first, rec, tid, ujs, b0, j0);
   if (n_el > kMThreads) {
     __syncthreads();   // waits for this wave's loads, then for the other waves
