@@ -49,24 +49,40 @@ __device__ __forceinline__ float tanh_f(float x) {
   return 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * x) + 1.f);
 }
 
-// The eleven ONNX activations in f32 (alpha, beta resolved by the caller).
+// The eleven ONNX activations in f32 (alpha, beta resolved by the caller),
+// one function per kind, and the same chosen at run time.
+template <int K>
+__device__ __forceinline__ float activate_k(float a, float b, float x) {
+  if constexpr (K == RNN_ACT_RELU) return x < 0.f ? 0.f : x;
+  else if constexpr (K == RNN_ACT_TANH) return tanh_f(x);
+  else if constexpr (K == RNN_ACT_SIGMOID) return sigmoid_f(x);
+  else if constexpr (K == RNN_ACT_AFFINE) return a * x + b;
+  else if constexpr (K == RNN_ACT_LEAKY_RELU) return x >= 0.f ? x : a * x;
+  else if constexpr (K == RNN_ACT_THRESHOLDED_RELU) return x > a ? x : 0.f;
+  else if constexpr (K == RNN_ACT_SCALED_TANH) return a * tanh_f(b * x);
+  else if constexpr (K == RNN_ACT_HARD_SIGMOID) {
+    float v = a * x + b;
+    v = v < 0.f ? 0.f : v;
+    return v > 1.f ? 1.f : v;
+  } else if constexpr (K == RNN_ACT_ELU) return x >= 0.f ? x : a * expm1f(x);
+  else if constexpr (K == RNN_ACT_SOFTSIGN) return x / (1.f + fabsf(x));
+  else if constexpr (K == RNN_ACT_SOFTPLUS) return (x > 0.f ? x : 0.f) + log1pf(expf(-fabsf(x)));  // log(1+e^x), overflow-free
+  else return __builtin_nanf("");
+}
+
 __device__ __forceinline__ float activate(int kind, float a, float b, float x) {
   switch (kind) {
-    case RNN_ACT_RELU: return x < 0.f ? 0.f : x;
-    case RNN_ACT_TANH: return tanh_f(x);
-    case RNN_ACT_SIGMOID: return sigmoid_f(x);
-    case RNN_ACT_AFFINE: return a * x + b;
-    case RNN_ACT_LEAKY_RELU: return x >= 0.f ? x : a * x;
-    case RNN_ACT_THRESHOLDED_RELU: return x > a ? x : 0.f;
-    case RNN_ACT_SCALED_TANH: return a * tanh_f(b * x);
-    case RNN_ACT_HARD_SIGMOID: {
-      float v = a * x + b;
-      v = v < 0.f ? 0.f : v;
-      return v > 1.f ? 1.f : v;
-    }
-    case RNN_ACT_ELU: return x >= 0.f ? x : a * expm1f(x);
-    case RNN_ACT_SOFTSIGN: return x / (1.f + fabsf(x));
-    case RNN_ACT_SOFTPLUS: return (x > 0.f ? x : 0.f) + log1pf(expf(-fabsf(x)));  // log(1+e^x), overflow-free
+    case RNN_ACT_RELU: return activate_k<RNN_ACT_RELU>(a, b, x);
+    case RNN_ACT_TANH: return activate_k<RNN_ACT_TANH>(a, b, x);
+    case RNN_ACT_SIGMOID: return activate_k<RNN_ACT_SIGMOID>(a, b, x);
+    case RNN_ACT_AFFINE: return activate_k<RNN_ACT_AFFINE>(a, b, x);
+    case RNN_ACT_LEAKY_RELU: return activate_k<RNN_ACT_LEAKY_RELU>(a, b, x);
+    case RNN_ACT_THRESHOLDED_RELU: return activate_k<RNN_ACT_THRESHOLDED_RELU>(a, b, x);
+    case RNN_ACT_SCALED_TANH: return activate_k<RNN_ACT_SCALED_TANH>(a, b, x);
+    case RNN_ACT_HARD_SIGMOID: return activate_k<RNN_ACT_HARD_SIGMOID>(a, b, x);
+    case RNN_ACT_ELU: return activate_k<RNN_ACT_ELU>(a, b, x);
+    case RNN_ACT_SOFTSIGN: return activate_k<RNN_ACT_SOFTSIGN>(a, b, x);
+    case RNN_ACT_SOFTPLUS: return activate_k<RNN_ACT_SOFTPLUS>(a, b, x);
     default: return __builtin_nanf("");
   }
 }

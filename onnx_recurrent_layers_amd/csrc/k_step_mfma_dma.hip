@@ -509,11 +509,60 @@ __device__ __forceinline__ void epi_tile_issue(const EpiCtx& c, const int* len_s
   }
 }
 
+// The elements after each thread's first of a plain RNN cell with a
+// non-default activation, its kind fixed at compile time: the same
+// arithmetic as epi_finish, without the activation's branches per element.
+template <typename RT, int K>
+__device__ __forceinline__ void rnn_tile_finish(const EpiCtx& c, const EpiIn& first, const int* len_s, const float* rec,
+                                                const float* planes, int n_el, int ujs, int b0, int j0) {
+  constexpr int LDR = kMaxNC + 1;
+  const int tid = threadIdx.x;
+  const int E = n_el / kMThreads;
+  const int UJ = 1 << ujs;
+  const int u = tid & (UJ - 1), j = j0 + u;
+  const int odd = j & 1;
+  const float wb = widen<RT>(first.wb[0], odd), rb = widen<RT>(first.rb[0], odd);
+  const float al = c.act[0].alpha, be = c.act[0].beta;
+  for (int k = 1; k < E; ++k) {
+    const int e = tid + k * kMThreads;
+    const int r = e >> ujs, b = b0 + r;
+    const int L = len_s[r];
+    if (!(b < c.B && j < c.H && c.s < L)) continue;
+    const float pre = pre_sum(planes[e], rec[r * LDR + u], wb, rb);
+    const float h = activate_k<K>(al, be, clipf(pre, c.clip));
+    epi_put_h(c, int64_t(b) * c.H + j, h);
+    epi_outputs<RT>(c, b, j, L, h, 0.f);
+  }
+}
+
 // Gate arithmetic of elements k = 1..E-1 from the planes; biases and
 // peepholes are those of the thread's first element (same unit).
-template <typename RT, bool DEF>
+template <typename RT, bool DEF, bool SPEC = false>
 __device__ __forceinline__ void epi_tile_finish(const EpiCtx& c, const EpiIn& first, const int* len_s, const float* rec,
                                                 const float* planes, int n_el, int ujs, int b0, int j0) {
+  // SPEC (the per-step kernel): a plain RNN cell takes a loop compiled for
+  // its activation kind
+  if constexpr (SPEC && !DEF) {
+    if (c.cell == RNN_CELL_RNN) {
+#define RNN_TILE_CASE(K) \
+  case K: rnn_tile_finish<RT, K>(c, first, len_s, rec, planes, n_el, ujs, b0, j0); return;
+      switch (c.act[0].kind) {
+        RNN_TILE_CASE(RNN_ACT_RELU)
+        RNN_TILE_CASE(RNN_ACT_TANH)
+        RNN_TILE_CASE(RNN_ACT_SIGMOID)
+        RNN_TILE_CASE(RNN_ACT_AFFINE)
+        RNN_TILE_CASE(RNN_ACT_LEAKY_RELU)
+        RNN_TILE_CASE(RNN_ACT_THRESHOLDED_RELU)
+        RNN_TILE_CASE(RNN_ACT_SCALED_TANH)
+        RNN_TILE_CASE(RNN_ACT_HARD_SIGMOID)
+        RNN_TILE_CASE(RNN_ACT_ELU)
+        RNN_TILE_CASE(RNN_ACT_SOFTSIGN)
+        RNN_TILE_CASE(RNN_ACT_SOFTPLUS)
+        default: break;
+      }
+#undef RNN_TILE_CASE
+    }
+  }
   const int tid = threadIdx.x;
   const int E = n_el / kMThreads;
   const int j = j0 + (tid & ((1 << ujs) - 1));
@@ -864,7 +913,7 @@ __device__ __forceinline__ void dma_step(const MfmaStepArgs& m, int s, int tx, i
   epi_finish<RT, DEF>(ctx, first, rec, tid, ujs, b0, j0);
   if (n_el > kMThreads) {
     __syncthreads();   // waits for this wave's loads, then for the other waves
-    epi_tile_finish<RT, DEF>(ctx, first, len_s, rec, planes, n_el, ujs, b0, j0);
+    epi_tile_finish<RT, DEF, !PERS>(ctx, first, len_s, rec, planes, n_el, ujs, b0, j0);
   }
 }
 
