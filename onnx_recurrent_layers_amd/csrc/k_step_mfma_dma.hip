@@ -523,6 +523,71 @@ __device__ __forceinline__ void rnn_tile_finish(const EpiCtx& c, const EpiIn& fi
   const int odd = j & 1;
   const float wb = widen<RT>(first.wb[0], odd), rb = widen<RT>(first.rb[0], odd);
   const float al = c.act[0].alpha, be = c.act[0].beta;
+  const bool quads = !c.coh && (c.H & 3) == 0 && (reinterpret_cast<uintptr_t>(c.hnext) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(c.hsn) & 7) == 0;
+  if (quads) {
+    // Four consecutive units of a row per thread and pass: the elements from
+    // row 256/UJ on (the rows of each thread's first element done), quad q of
+    // them at row 256/UJ + q/QR, units 4(q % QR) ..; a thread keeps its four
+    // units (256 is a multiple of QR), so it loads their biases once.  One
+    // 16-byte LDS read for their Xw, and h, its halves and Y written with
+    // one store each per quad; the arithmetic per element is that of the
+    // loop below.
+    const int QR = UJ >> 2;
+    const int uq = 4 * (tid & (QR - 1)), jq = j0 + uq;
+    const int r0 = kMThreads >> ujs;
+    const int nq = (n_el - kMThreads) >> 2;
+    float wq[4], rq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = c.gate[0] * c.H + jq + i, odd = (jq + i) & 1;
+      wq[i] = jq + i < c.H ? widen<RT>(res_load<RT>(c.bias, n), odd) : 0.f;
+      rq[i] = jq + i < c.H ? widen<RT>(res_load<RT>(c.bias, c.GH + n), odd) : 0.f;
+    }
+    const bool yvec = c.Y && (reinterpret_cast<uintptr_t>(c.Y) & (4 * sizeof(RT) - 1)) == 0;
+    for (int q = tid; q < nq; q += kMThreads) {
+      const int r = r0 + q / QR, b = b0 + r;
+      const int L = len_s[r];
+      if (!(b < c.B && jq < c.H && c.s < L)) continue;
+      const f32x4 xq = *reinterpret_cast<const f32x4*>(planes + (r << ujs) + uq);
+      const float* rr = rec + r * LDR + uq;
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h[i] = activate_k<K>(al, be, clipf(pre_sum(xq[i], rr[i], wq[i], rq[i]), c.clip));
+      const int64_t si = int64_t(b) * c.H + jq;
+      *reinterpret_cast<f32x4*>(c.hnext + si) = f32x4{h[0], h[1], h[2], h[3]};
+      if (c.hsn) {
+        unsigned short hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_bits(c.split_kind, h[i], hi[i], lo[i]);
+        typedef unsigned short us4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<us4*>(c.hsn + si) = us4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<us4*>(c.hsn + si + c.DBH) = us4{lo[0], lo[1], lo[2], lo[3]};
+      }
+      if (yvec) {
+        const int t = c.rev ? (L - 1 - c.s) : c.s;
+        RT* y = static_cast<RT*>(c.Y) + y_index(c.layout, c.S, c.D, c.B, c.H, t, c.d, b, jq);
+        if constexpr (sizeof(RT) == 4) {
+          *reinterpret_cast<f32x4*>(y) = f32x4{h[0], h[1], h[2], h[3]};
+        } else {
+          typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<h4v*>(y) = h4v{_Float16(h[0]), _Float16(h[1]), _Float16(h[2]), _Float16(h[3])};
+        }
+        if (c.s == L - 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t hi2 = state_index(c.layout, c.D, c.B, c.H, c.d, b, jq + i);
+            if (c.Y_h) static_cast<RT*>(c.Y_h)[hi2] = to_elem<RT>(h[i]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) epi_outputs<RT>(c, b, jq + i, L, h[i], 0.f);
+      }
+    }
+    return;
+  }
   for (int k = 1; k < E; ++k) {
     const int e = tid + k * kMThreads;
     const int r = e >> ujs, b = b0 + r;

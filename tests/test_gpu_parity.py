@@ -606,8 +606,11 @@ ALL_ACTS = [("Relu", 0, 0), ("Tanh", 0, 0), ("Sigmoid", 0, 0), ("Affine", 0.7, -
 
 # A plain RNN cell on tiles with several elements per thread (64x64 and
 # 32x16 tiles, forced) takes, in the one-launch-per-step kernel, an epilogue
-# loop compiled for its activation kind: every kind, in each direction, in the
-# f32 matrix-core mode and the bf16 split mode, ragged batch and hidden.
+# loop compiled for its activation kind, and with hidden a multiple of 4 its
+# four-units-per-thread form (vector stores of h, its halves and Y): every
+# kind, in each direction, in the f32 matrix-core mode and the bf16 split
+# mode, f32 and f16 tensors, ragged batch, hidden not a multiple of 4, and Y
+# and Y_h at odd element offsets (no vector store of Y).
 RNN_TILE_ACTS = [(k, ALL_ACTS[k], ALL_ACTS[(k + 5) % len(ALL_ACTS)]) for k in range(len(ALL_ACTS))]
 
 
@@ -615,11 +618,14 @@ RNN_TILE_ACTS = [(k, ALL_ACTS[k], ALL_ACTS[(k + 5) % len(ALL_ACTS)]) for k in ra
 def test_rnn_large_tile_activations(k, fwd, rev, monkeypatch):
     monkeypatch.setenv("RNN_MFMA_TILE", "64x64" if k % 2 == 0 else "32x16")
     monkeypatch.setenv("RNN_F32_SPLIT", "1" if k % 3 == 0 else "0")
-    spec = LayerSpec("RNN", seq=5, batch=70, input=24, hidden=100 if k % 2 == 0 else 92, direction="bidirectional", dtype="f32",
+    hidden = (100, 92, 98)[k % 3]
+    dtype = "f16" if k % 4 == 3 else "f32"
+    spec = LayerSpec("RNN", seq=5, batch=70, input=24, hidden=hidden, direction="bidirectional", dtype=dtype,
                      acts=(fwd, rev), init_h=True, lens=True, clip=3.0 if k % 4 == 1 else None,
                      outputs=("Y", "Y_h"))
     inp = make_inputs(spec, 61 + k, Dists(sequence_lens=("I", 0, 5), W=("U", -0.3, 0.3), R=("U", -0.2, 0.2)))
-    check(spec, inp, engine="launch", what=f"RNN large tile {fwd[0]}/{rev[0]}")
+    offsets = {"Y": 3, "Y_h": 5} if k % 5 == 2 else None
+    check(spec, inp, engine="launch", offsets=offsets, what=f"RNN large tile {fwd[0]}/{rev[0]} {dtype} H{hidden}")
 
 
 @pytest.mark.parametrize("engine", ENGINES)
