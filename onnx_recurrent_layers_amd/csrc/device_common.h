@@ -162,6 +162,13 @@ __device__ __forceinline__ const float* xw_slab(const StepArgs& a, int d, int s)
   return a.xw + ((int64_t(q & 1) * a.D + d) * a.xw_tc + (s - q * a.xw_tc)) * int64_t(a.B) * (a.G * a.H);
 }
 
+// Direction d's first slab when the projection scratch is one slot of every
+// step (the persistent engines): step s's slab follows it at s * B * G * H,
+// an address with no division in it.
+__device__ __forceinline__ const float* xw_dir(const StepArgs& a, int d) {
+  return a.xw + int64_t(d) * a.xw_tc * int64_t(a.B) * (a.G * a.H);
+}
+
 // Index of a state tensor (initial_h, initial_c, Y_h, Y_c) for direction d,
 // batch row b, unit j: layout 0 [D][B][H], layout 1 [B][D][H].
 __device__ __forceinline__ int64_t state_index(int layout, int D, int B, int H, int d, int b, int j) {

@@ -612,7 +612,7 @@ __device__ __forceinline__ int fallback_blocks(const PersArgs& p, int d, unsigne
         if (!(g_uu < Uw && g_b < B && s < L)) continue;
         const int64_t si = dBH + int64_t(g_b) * H + j;
         const int t = rev ? L - 1 - s : s;
-        const float* xw = xw_slab(a, d, s) + int64_t(g_b) * GH + j;
+        const float* xw = xw_dir(a, d) + (int64_t(s) * B + g_b) * GH + j;
         float xv[4] = {0.f, 0.f, 0.f, 0.f}, wb[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
         float peep[3] = {0.f, 0.f, 0.f};
         for (int g = 0; g < G; ++g) {
@@ -776,14 +776,16 @@ __global__ __launch_bounds__(kPThreads) void persistent_kernel(PersArgs p) {
   // it): a load under a lane condition makes the compiler copy the
   // registers and wait for every memory operation issued after it, the
   // exchange stores included, whose completion takes a long trip.
+  const int64_t xw_stride = int64_t(B) * GH;   // one step's slab
+  const float* xw_me = xw_dir(a, d) + int64_t(min(g_b, B - 1)) * GH + min(j, H - 1);
   auto fetch_xw = [&](int step, float* out) {
     if constexpr (MF) {
       const int st = max(0, min(step, L - 1));
-      const float* xw = xw_slab(a, d, st) + int64_t(min(g_b, B - 1)) * GH + min(j, H - 1);
+      const float* xw = xw_me + st * xw_stride;
 #pragma unroll
       for (int g = 0; g < 4; ++g) out[g] = xw[min(g, G - 1) * H];
     } else if (gthread && step < L) {
-      const float* xw = xw_slab(a, d, step) + int64_t(g_b) * GH + j;
+      const float* xw = xw_me + step * xw_stride;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         if (g < G && !(a.input_forget && g == 2)) out[g] = xw[g * H];
