@@ -288,7 +288,12 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
     proj_kind = rl.PRODUCTS[plan.proj_products]
 
     step_launches = max(1, plan.step_launches)
-    launch_ms = st["steps"] / step_launches
+    # A projection in chunks: the projection stage times the first chunk; the
+    # later ones run inside the steps stage, each about as long as the first.
+    tc = plan.xw_chunk_steps
+    nchunks = -(-n_steps // tc) if 0 < tc < n_steps else 1
+    steps_only_ms = st["steps"] - (nchunks - 1) * st["projection"]
+    launch_ms = steps_only_ms / step_launches
     per_step_us = st["steps"] * 1000.0 / max(1, n_steps)
     bytes_per_launch = step_bytes(spec) * n_steps / step_launches
     hbm = bytes_per_launch / (launch_ms / 1000.0) / 1e9
@@ -316,6 +321,9 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
         "step_products": step_kind, "step_bounds": bounds, "fallback_workgroups": run.fallback_workgroups,
         "xw_chunk_steps": plan.xw_chunk_steps, "xw_slots": plan.xw_slots, "xw_scratch_bytes": layer.xw_bytes,
     }
+    if nchunks > 1:
+        res["step_launch_us_what"] = ("steps stage less the %d later projection chunks (each taken as long as the "
+                                      "first, which the projection stage times), over the step launches" % (nchunks - 1))
     if floors and engine_name == "persistent" and plan.step_products in (0, 2) and spec.batch <= 8:
         fl = step_floors(spec, dt)
         res["step_floor"] = fl
@@ -327,11 +335,14 @@ def measure(name: str, engine: str, K: int, warmup: int, floors: bool, cpu_secon
                     "workgroup barriers and the gate chain"}
     # the binding bound: the largest fraction
     res["binding"] = max(res["step_bounds"], key=lambda k: res["step_bounds"][k]["frac"])
-    pm = proj_flops(spec)
+    pm = proj_flops(spec) * (min(tc, n_steps) / n_steps if nchunks > 1 else 1.0)
     pi = pm * ISSUED_PER_PRODUCT[proj_kind]
     pt = st["projection"]
     res["projection"] = {
         "units": proj_kind, "method_flops": pm, "issued_flops": pi, "ms": round(pt, 5),
+        "chunks": nchunks,
+        "what": ("the first of %d chunks of %d steps (its flops over the projection stage's time; the later "
+                 "chunks run between the steps)" % (nchunks, tc)) if nchunks > 1 else "the whole projection",
         "method_tflops": round(pm / (pt / 1e3) / 1e12, 3) if pt > 0 else 0.0,
         "issued_tflops": round(pi / (pt / 1e3) / 1e12, 3) if pt > 0 else 0.0,
         "peak_tflops": PEAK_TFLOPS[proj_kind],
