@@ -155,6 +155,8 @@ struct EpiCtx {
   const float* xw;      // the projection slab of this step and direction, [B][G*H]
   const float* hprev;   // h of this step, [B][H]
   float* hnext;         // h of the next step, [B][H]
+  bool h32;             // hnext is written: its readers are the f32 mode's product and the GRU gates;
+                        // the other cells of the split modes read h only as 16-bit halves
   void* Y;              // outputs (or null), written as the step finishes each element
   void* Y_h;
   void* Y_c;
@@ -218,6 +220,9 @@ __device__ __forceinline__ EpiCtx epi_context(const MfmaStepArgs& m, int d, int 
   c.cst = a.cell_state + dBH;
   c.DBH = DBH;
   c.hsn = a.hsplit ? a.hsplit + int64_t((step + 1) & 1) * 2 * DBH + dBH : nullptr;
+  // (the persistent form keeps the store: without it C4's shape measured
+  // slower, its schedule being what it is)
+  c.h32 = coh || !c.hsn || a.cell == RNN_CELL_GRU;
   c.rhs = a.rhsplit ? a.rhsplit + dBH : nullptr;
   c.split_kind = a.split_kind;
   c.zbuf = a.zbuf + dBH;
@@ -330,7 +335,7 @@ __device__ __forceinline__ void epi_gather(const EpiCtx& c, const int* len_s, in
 
 // h of the next step: f32, and in mode 2 also its bf16 planes.
 __device__ __forceinline__ void epi_put_h(const EpiCtx& c, int64_t si, float h) {
-  st_st(c.hnext + si, h, c.coh);
+  if (c.h32) st_st(c.hnext + si, h, c.coh);
   if (c.hsn) st_split(c.hsn + si, c.DBH, h, c.coh, c.split_kind);
 }
 
@@ -556,7 +561,7 @@ __device__ __forceinline__ void rnn_tile_finish(const EpiCtx& c, const EpiIn& fi
       for (int i = 0; i < 4; ++i)
         h[i] = activate_k<K>(al, be, clipf(pre_sum(xq[i], rr[i], wq[i], rq[i]), c.clip));
       const int64_t si = int64_t(b) * c.H + jq;
-      *reinterpret_cast<f32x4*>(c.hnext + si) = f32x4{h[0], h[1], h[2], h[3]};
+      if (c.h32) *reinterpret_cast<f32x4*>(c.hnext + si) = f32x4{h[0], h[1], h[2], h[3]};
       if (c.hsn) {
         unsigned short hi[4], lo[4];
 #pragma unroll
