@@ -962,13 +962,17 @@ bool persistent_supported(const Problem& p, int* blocks, int* units, int* wg_per
   const int Gp = p.G - ((p.desc.cell == RNN_CELL_LSTM && p.desc.input_forget) ? 1 : 0);
   const int NB = next_pow2_nb(int(p.B));
   const int maxw = 256 / p.D;  // one workgroup per compute unit
-  // R rows per workgroup: about 16 for the vector-ALU products (more
-  // workgroups share each step's products: C2 3.54 us per step at 16 rows
-  // against 3.73 at 32 and 3.76 at 64), about 64 for the matrix-core products
-  // (16-row blocks; C3 is 4 % slower at 24 rows than at 48 or 63).
+  // R rows per workgroup: about 16.  The vector-ALU products: more
+  // workgroups share each step's products (C2 3.54 us per step at 16 rows
+  // against 3.73 at 32 and 3.76 at 64).  The matrix-core products work in
+  // blocks of 16 rows, and a second block costs more than the extra
+  // workgroups: biGRU seq 128, batch 8, hidden 512, f16 with
+  // linear_before_reset = 1 took 494 us of steps at 12 or 15 rows (4 or 5
+  // units) against 524 us at 18 or 24; with linear_before_reset = 0 (two
+  // phases of 2U and U rows) 854 us either way.
   // RNN_PERSISTENT_UNITS overrides the choice for tuning.
-  const bool mf_rows = p.esize == 2 && NB >= 4 && default_acts(p);
-  int U = std::max(1, (mf_rows ? 64 : 16) / Gp);
+  const bool mf_rows = p.esize == 2 && NB >= 4 && default_acts(p);   // the matrix-core products
+  int U = std::max(1, 16 / Gp);
   if (const char* env = std::getenv("RNN_PERSISTENT_UNITS")) U = std::max(1, std::atoi(env));
   U = std::min(U, 64 / NB);
   int wpd = int((p.H + U - 1) / U);
