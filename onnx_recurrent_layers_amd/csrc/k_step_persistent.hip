@@ -179,7 +179,7 @@ __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, cons
 // and variants for more slots cost every kernel registers, so larger layers
 // keep one batch at a time.
 constexpr int kPollStagger = 32;   // s_sleep units of 64 cycles: about 0.85 us
-constexpr int kPollDelayMF = 16;   // before the first poll of the matrix-core form: about 0.43 us
+constexpr int kPollDelayMF = 24;   // before the first poll of the matrix-core form: about 0.64 us
 
 // One batch row of up to 2 * kPollThreads units (the f32 copy of h is then
 // h itself): polling thread t watches words t and t + kPollThreads.
@@ -242,9 +242,10 @@ __device__ __forceinline__ int stage_words(const unsigned long long* src, void* 
   int fail = 0;
   const int lo = NB * HS;
   WordPoll w;
-  // with the matrix-core products, a first poll about 0.4 us late sees more
-  // words landed (C3: 929 -> 899 us, its linear_before_reset form 578 -> 553;
-  // 0.64 us gained less, 0.85 us lost)
+  // with the matrix-core products, a first poll about 0.64 us late sees more
+  // words landed (biGRU seq 128 batch 8 hidden 512 f16 at about 16 R rows per
+  // workgroup: steps 976 us without the pause, 855 at 0.43 us, 849 at 0.64 us,
+  // 890 at 0.85 us; with linear_before_reset = 1: 574, 495, 473, 477 us)
   if constexpr (MF) __builtin_amdgcn_s_sleep(kPollDelayMF);
   poll_issue(w, m0, src, ptid, amask);
   fail |= poll_complete<MF>(w, m0, src, ptid, hs, lo, tag);
