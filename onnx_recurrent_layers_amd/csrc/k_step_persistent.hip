@@ -178,7 +178,10 @@ __device__ __forceinline__ int poll_complete(WordPoll& w, const WordMap& m, cons
 // traffic swamps the memory system (22 words per thread: 3.6 times slower),
 // and variants for more slots cost every kernel registers, so larger layers
 // keep one batch at a time.
-constexpr int kPollStagger = 32;   // s_sleep units of 64 cycles: about 0.85 us
+// s_sleep units of 64 cycles: about 0.9 us.  The optimum is narrow: biLSTM
+// seq 80 batch 1 hidden 256 f32 took 194.5, 186.8, 180.1, 178.8 and 182.6 us
+// of steps at 28, 30, 32, 34 and 36.
+constexpr int kPollStagger = 34;
 constexpr int kPollDelayMF = 24;   // before the first poll of the matrix-core form: about 0.64 us
 
 // One batch row of up to 2 * kPollThreads units (the f32 copy of h is then
